@@ -1,0 +1,808 @@
+/*
+ * fp4q_ref.c -- CPU oracle for block-scaled 4-bit quantization.
+ *
+ * TEST INFRASTRUCTURE ONLY (see fp4q_ref.h).  Plain scalar C, one block at a
+ * time, in the order the method states.  Built with -O2 -ffp-contract=off
+ * and without fast-math, so every float operation below is one IEEE
+ * binary32 operation and every double operation one binary64 operation.
+ *
+ * The method, step by step, with the page each step follows:
+ *   1. widen bf16 to f32 (exact);
+ *   2. optional block Hadamard along the contiguous axis, block length n
+ *      equal to the quantization block   [MR, Method 1: block-wise Hadamard];
+ *   3. NVFP4 / IF4: global scale S = max|x| / (256*6)
+ *                                         [SS, Method 2: global scale];
+ *   4. per block: AbsMax base scale s_base = E4M3(max|x| / (6 S))
+ *      ("block max rounded to FP8")       [SS, Method 2: upper bound];
+ *   5. candidates: AbsMax -> {s_base}; ScaleSweep -> the E4M3 bit patterns
+ *      s_base + k, k in [lo, hi] ([-3,7] for MSE, [-8,7] for WMSE)
+ *                                         [SS, Method 2 and 3];
+ *   6. encode each element to the nearest E2M1 value of |x| / (s S);
+ *   7. keep the candidate of least block error, MSE or importance-weighted
+ *      MSE                                [SS, Method 1: objectives];
+ *   8. IF4: compare the FP4 encoding with a scaled INT4 encoding whose step
+ *      carries the 6/7 factor, keep the lower MSE and record the choice in
+ *      the scale's sign bit               [IF4, Methodology];
+ *   9. MXFP4: one E8M0 power-of-two scale per 32 elements, no global scale
+ *                                         [MR, Problem].
+ *
+ * Readings taken where the pages are silent (each is listed in the design
+ * notes): E2M1 and INT4 rounding is round-to-nearest with ties to the even
+ * code and saturation at the largest magnitude; the sign of a zero code is
+ * the sign of the input; every scale computation is the binary32 sequence
+ * written below (D = s*S, r = 1/D, y = |x|*r); block errors are evaluated in
+ * binary64, and exact ties keep the smaller scale byte (the FP4 branch for
+ * IF4); the sweep offset is added to the 7-bit E4M3 magnitude pattern and
+ * patterns outside [0x01, 0x7E] are skipped; S = 1 for an all-zero tensor
+ * and S is never below 2^-117 so that every candidate reciprocal is finite;
+ * the MXFP4 exponent is floor(log2 max|x|) - 2 clamped to [-127, 127]; the
+ * Hadamard is the Sylvester (natural-order) matrix evaluated by butterflies
+ * with stage widths 1, 2, 4, ..., n/2 and then scaled by fl32(1/sqrt(n)).
+ */
+#include "fp4q_ref.h"
+
+#include <math.h>
+#include <pthread.h>
+#include <stdlib.h>
+#include <string.h>
+#include <unistd.h>
+
+/* ------------------------------------------------------------------------ */
+/* formats                                                                  */
+/* ------------------------------------------------------------------------ */
+
+/* E2M1: one sign bit (carried separately), two exponent bits with bias 1,
+ * one mantissa bit; exponent field 0 is subnormal.  Largest magnitude 6
+ * [IF4, Problem: FP4's maximum is 6]. */
+float fp4q_ref_e2m1_value(int m)
+{
+    int e = (m >> 1) & 3;
+    int f = m & 1;
+    if (e == 0)
+        return (float)(0.5 * f);
+    return (float)ldexp(1.0 + 0.5 * f, e - 1);
+}
+
+/* nearest E2M1 magnitude to y >= 0; on an exact tie the even code wins.
+ * Above 6 the nearest value is 6, which is the saturating behaviour. */
+int fp4q_ref_e2m1_round(float y)
+{
+    if (y >= 6.0f) /* also catches +inf, whose distance to every value is inf */
+        return 7;
+    int best = 0;
+    double bestd = INFINITY;
+    for (int m = 0; m < 8; ++m) {
+        double d = fabs((double)y - (double)fp4q_ref_e2m1_value(m));
+        if (d < bestd || (d == bestd && (m & 1) == 0 && (best & 1) == 1)) {
+            best = m;
+            bestd = d;
+        }
+    }
+    return best;
+}
+
+/* E4M3FN (OCP FP8): sign, 4 exponent bits with bias 7, 3 mantissa bits,
+ * exponent field 0 subnormal, 0x7F / 0xFF are NaN, no infinities.  Bytes
+ * 0x01..0x7E are the 126 positive finite values [SS, Method 2]. */
+float fp4q_ref_e4m3_value(int byte)
+{
+    int b = byte & 0x7F;
+    double sgn = (byte & 0x80) ? -1.0 : 1.0;
+    if (b == 0x7F)
+        return NAN;
+    int e = b >> 3;
+    int f = b & 7;
+    if (e == 0)
+        return (float)(sgn * ldexp((double)f, -9));
+    return (float)(sgn * ldexp((double)(8 + f), e - 10));
+}
+
+/* nearest non-negative E4M3 value to t >= 0, ties to the even byte, with
+ * saturation at 448 (0x7E): the nearest finite value to anything above 448
+ * is 448 itself. */
+int fp4q_ref_e4m3_round(float t)
+{
+    if (t >= 448.0f)
+        return 0x7E;
+    int best = 0;
+    double bestd = INFINITY;
+    for (int b = 0; b <= 0x7E; ++b) {
+        double d = fabs((double)t - (double)fp4q_ref_e4m3_value(b));
+        if (d < bestd || (d == bestd && (b & 1) == 0 && (best & 1) == 1)) {
+            best = b;
+            bestd = d;
+        }
+    }
+    return best;
+}
+
+/* E8M0: an unsigned biased power of two, 2^(byte-127); 0xFF is NaN. */
+float fp4q_ref_e8m0_value(int byte)
+{
+    if ((byte & 0xFF) == 0xFF)
+        return NAN;
+    return (float)ldexp(1.0, (byte & 0xFF) - 127);
+}
+
+/* nearest integer in 0..7 to y >= 0, ties to even, saturating at 7 */
+int fp4q_ref_int4_round(float y)
+{
+    if (y >= 7.0f)
+        return 7;
+    int best = 0;
+    double bestd = INFINITY;
+    for (int q = 0; q <= 7; ++q) {
+        double d = fabs((double)y - (double)q);
+        if (d < bestd || (d == bestd && (q & 1) == 0 && (best & 1) == 1)) {
+            best = q;
+            bestd = d;
+        }
+    }
+    return best;
+}
+
+float fp4q_ref_bf16_to_f32(uint16_t h)
+{
+    uint32_t u = (uint32_t)h << 16;
+    float f;
+    memcpy(&f, &u, 4);
+    return f;
+}
+
+/* bf16 keeps the top 16 bits of a binary32: choose the nearer of the two
+ * truncations that bracket f, the one with an even last bit on a tie. */
+uint16_t fp4q_ref_f32_to_bf16(float f)
+{
+    uint32_t u;
+    memcpy(&u, &f, 4);
+    if (isnan(f))
+        return (uint16_t)((u >> 16) | 0x0040);
+    uint32_t lo = u & 0xFFFF0000u;   /* truncation toward zero */
+    uint32_t hi = lo + 0x00010000u;  /* next bf16 away from zero */
+    float flo;
+    memcpy(&flo, &lo, 4);
+    double vlo = (double)flo;
+    double vhi;
+    if ((hi & 0x7F800000u) == 0x7F800000u) {
+        /* the step past the largest finite bf16 lands on 2^128 */
+        vhi = copysign(ldexp(1.0, 128), (double)f);
+    } else {
+        float fhi;
+        memcpy(&fhi, &hi, 4);
+        vhi = (double)fhi;
+    }
+    double dlo = fabs((double)f - vlo);
+    double dhi = fabs(vhi - (double)f);
+    if (dlo < dhi)
+        return (uint16_t)(lo >> 16);
+    if (dhi < dlo)
+        return (uint16_t)(hi >> 16);
+    return (uint16_t)((((lo >> 16) & 1) == 0 ? lo : hi) >> 16);
+}
+
+/* the INT4 step factor of the 6/7 method [IF4, Methodology]: INT4 codes
+ * 0..7 are stretched so that 7 lands where FP4's 6 does. */
+float fp4q_ref_int4_step(void)
+{
+    return 6.0f / 7.0f;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Hadamard and global scale                                                */
+/* ------------------------------------------------------------------------ */
+
+float fp4q_ref_rotation_scale(int n)
+{
+    return (float)(1.0 / sqrt((double)n));
+}
+
+/* y = H_n x / sqrt(n) for the Sylvester matrix H_n[i][j] = (-1)^popcount(i&j),
+ * evaluated as log2(n) butterfly stages of widths 1, 2, ..., n/2 followed by
+ * one multiplication [MR, Method 1: block-wise Hadamard before quantizing]. */
+void fp4q_ref_fwht(float* v, int n)
+{
+    for (int h = 1; h < n; h *= 2) {
+        for (int i = 0; i < n; i += 2 * h) {
+            for (int j = i; j < i + h; ++j) {
+                float a = v[j];
+                float b = v[j + h];
+                v[j] = a + b;
+                v[j + h] = a - b;
+            }
+        }
+    }
+    float c = fp4q_ref_rotation_scale(n);
+    for (int k = 0; k < n; ++k)
+        v[k] = v[k] * c;
+}
+
+/* S = max|x| / (256*6) [SS, Method 2: global scale]; 1 for an all-zero
+ * tensor, and at least 2^-117 so that D = s*S >= 2^-126 for every E4M3
+ * byte and 1/D stays finite. */
+float fp4q_ref_global_scale(float g)
+{
+    if (g == 0.0f)
+        return 1.0f;
+    float s = g / 1536.0f;
+    float floor_s = (float)ldexp(1.0, -117);
+    return s < floor_s ? floor_s : s;
+}
+
+/* ------------------------------------------------------------------------ */
+/* a tiny row-range thread pool                                             */
+/* ------------------------------------------------------------------------ */
+
+typedef void (*row_fn)(void* ctx, int64_t r0, int64_t r1);
+
+typedef struct {
+    row_fn fn;
+    void* ctx;
+    int64_t r0, r1;
+} row_job;
+
+static void* row_job_run(void* p)
+{
+    row_job* j = (row_job*)p;
+    j->fn(j->ctx, j->r0, j->r1);
+    return NULL;
+}
+
+static int resolve_threads(int nthreads)
+{
+    if (nthreads > 0)
+        return nthreads;
+    long n = sysconf(_SC_NPROCESSORS_ONLN);
+    return n > 0 ? (int)n : 1;
+}
+
+static void parallel_rows(int64_t rows, int nthreads, row_fn fn, void* ctx)
+{
+    int nt = resolve_threads(nthreads);
+    if (nt > rows)
+        nt = rows > 0 ? (int)rows : 1;
+    if (nt <= 1) {
+        fn(ctx, 0, rows);
+        return;
+    }
+    pthread_t* th = (pthread_t*)malloc(sizeof(pthread_t) * (size_t)nt);
+    row_job* jobs = (row_job*)malloc(sizeof(row_job) * (size_t)nt);
+    for (int t = 0; t < nt; ++t) {
+        jobs[t].fn = fn;
+        jobs[t].ctx = ctx;
+        jobs[t].r0 = rows * t / nt;
+        jobs[t].r1 = rows * (t + 1) / nt;
+        pthread_create(&th[t], NULL, row_job_run, &jobs[t]);
+    }
+    for (int t = 0; t < nt; ++t)
+        pthread_join(th[t], NULL);
+    free(th);
+    free(jobs);
+}
+
+/* ------------------------------------------------------------------------ */
+/* widening and rotation                                                    */
+/* ------------------------------------------------------------------------ */
+
+typedef struct {
+    const void* x;
+    int dtype;
+    int64_t cols;
+    int rotate;
+    float* out;
+} prep_ctx;
+
+static void prep_rows(void* p, int64_t r0, int64_t r1)
+{
+    prep_ctx* c = (prep_ctx*)p;
+    for (int64_t r = r0; r < r1; ++r) {
+        float* o = c->out + r * c->cols;
+        for (int64_t j = 0; j < c->cols; ++j) {
+            int64_t k = r * c->cols + j;
+            if (c->dtype == REF_BF16)
+                o[j] = fp4q_ref_bf16_to_f32(((const uint16_t*)c->x)[k]);
+            else
+                o[j] = ((const float*)c->x)[k];
+        }
+        if (c->rotate > 0)
+            for (int64_t j = 0; j < c->cols; j += c->rotate)
+                fp4q_ref_fwht(o + j, c->rotate);
+    }
+}
+
+int fp4q_ref_prepare(const void* x, int x_dtype, int64_t rows, int64_t cols,
+                     int rotate, float* out, int nthreads)
+{
+    if (!x || !out || rows < 0 || cols < 0)
+        return -1;
+    if (x_dtype != REF_F32 && x_dtype != REF_BF16)
+        return -2;
+    if (rotate != 0 && (rotate < 2 || (rotate & (rotate - 1)) || cols % rotate))
+        return -2;
+    prep_ctx c = {x, x_dtype, cols, rotate, out};
+    parallel_rows(rows, nthreads, prep_rows, &c);
+    return 0;
+}
+
+/* ------------------------------------------------------------------------ */
+/* per-block encoders                                                       */
+/* ------------------------------------------------------------------------ */
+
+static float block_absmax(const float* xb, int B)
+{
+    float a = 0.0f;
+    for (int i = 0; i < B; ++i) {
+        float v = fabsf(xb[i]);
+        if (v > a)
+            a = v;
+    }
+    return a;
+}
+
+int fp4q_ref_base_scale(const float* xb, int B, float S)
+{
+    float a = block_absmax(xb, B);
+    if (a == 0.0f)
+        return 0;
+    float s6 = 6.0f * S;
+    int sb = fp4q_ref_e4m3_round(a / s6);
+    return sb == 0 ? 1 : sb;
+}
+
+/* squared error of one element, weighted when w != NULL, in binary64 */
+static double elem_err(float a, float xh, const float* w, int i)
+{
+    double d = (double)a - (double)xh;
+    double t = d * d;
+    if (w)
+        t = (double)w[i] * t;
+    return t;
+}
+
+double fp4q_ref_nvfp4_block(const float* xb, int B, const float* w, float S,
+                            int c, uint8_t* codes)
+{
+    float s = fp4q_ref_e4m3_value(c);
+    float D = s * S;
+    float r = 1.0f / D;
+    double E = 0.0;
+    for (int i = 0; i < B; ++i) {
+        float a = fabsf(xb[i]);
+        float y = a * r;
+        int m = fp4q_ref_e2m1_round(y);
+        float xh = fp4q_ref_e2m1_value(m) * D;
+        E = E + elem_err(a, xh, w, i);
+        if (codes)
+            codes[i] = (uint8_t)((signbit(xb[i]) ? 8 : 0) | m);
+    }
+    return E;
+}
+
+double fp4q_ref_int4_block(const float* xb, int B, const float* w, float S,
+                           int c, uint8_t* codes)
+{
+    float s = fp4q_ref_e4m3_value(c);
+    float D = s * S;
+    float Di = D * fp4q_ref_int4_step();
+    float ri = 1.0f / Di;
+    double E = 0.0;
+    for (int i = 0; i < B; ++i) {
+        float a = fabsf(xb[i]);
+        float y = a * ri;
+        int q = fp4q_ref_int4_round(y);
+        float xh = (float)q * Di;
+        E = E + elem_err(a, xh, w, i);
+        if (codes) {
+            int sq = signbit(xb[i]) ? -q : q;
+            codes[i] = (uint8_t)(sq & 0xF);
+        }
+    }
+    return E;
+}
+
+typedef struct {
+    const float* xb;
+    int B;
+    const float* w;
+    float S;
+    double* out;
+} cand_ctx;
+
+static void cand_rows(void* p, int64_t b0, int64_t b1)
+{
+    cand_ctx* c = (cand_ctx*)p;
+    for (int64_t b = b0; b < b1; ++b) {
+        const float* xb = c->xb + b * c->B;
+        const float* w = c->w ? c->w + b * c->B : NULL;
+        double* o = c->out + b * 127;
+        o[0] = NAN;
+        for (int s = 1; s <= 0x7E; ++s)
+            o[s] = fp4q_ref_nvfp4_block(xb, c->B, w, c->S, s, NULL);
+    }
+}
+
+int fp4q_ref_candidate_errors(const float* xb, int64_t nblocks, int B,
+                              const float* w, float S, double* out, int nthreads)
+{
+    if (!xb || !out || nblocks < 0 || B <= 0)
+        return -1;
+    cand_ctx c = {xb, B, w, S, out};
+    parallel_rows(nblocks, nthreads, cand_rows, &c);
+    return 0;
+}
+
+/* floor(log2(a)) for a > 0, subnormals included */
+static int floor_log2(float a)
+{
+    int e;
+    double m = frexp((double)a, &e); /* a = m 2^e, m in [0.5, 1) */
+    (void)m;
+    return e - 1;
+}
+
+/* ------------------------------------------------------------------------ */
+/* quantize                                                                 */
+/* ------------------------------------------------------------------------ */
+
+typedef struct {
+    int format, block, rule, objective, lo, hi;
+    const float* xr; /* widened, rotated */
+    int64_t cols;
+    const float* imp;
+    float S;
+    uint8_t* codes;
+    uint8_t* scales;
+    double* best;
+    double* second;
+} quant_ctx;
+
+static void put_nibbles(uint8_t* codes, int64_t elem0, const uint8_t* nib, int B)
+{
+    for (int i = 0; i < B; i += 2)
+        codes[(elem0 + i) / 2] = (uint8_t)((nib[i] & 0xF) | ((nib[i + 1] & 0xF) << 4));
+}
+
+static void quant_rows(void* p, int64_t r0, int64_t r1)
+{
+    quant_ctx* q = (quant_ctx*)p;
+    const int B = q->block;
+    const int64_t nbr = q->cols / B;
+    uint8_t nib[64], tmp[64];
+    for (int64_t r = r0; r < r1; ++r) {
+        for (int64_t jb = 0; jb < nbr; ++jb) {
+            int64_t e0 = r * q->cols + jb * B;
+            int64_t bi = r * nbr + jb;
+            const float* xb = q->xr + e0;
+            const float* w = (q->objective == REF_WMSE) ? q->imp + jb * B : NULL;
+            double best = 0.0, second = INFINITY;
+            uint8_t sbyte = 0;
+            float a = block_absmax(xb, B);
+
+            if (q->format == REF_MXFP4) {
+                int e = (a == 0.0f) ? -127 : floor_log2(a) - 2;
+                if (e < -127) e = -127;
+                if (e > 127) e = 127;
+                sbyte = (uint8_t)(e + 127);
+                float D = (float)ldexp(1.0, e);
+                float rr = (float)ldexp(1.0, -e);
+                best = 0.0;
+                for (int i = 0; i < B; ++i) {
+                    float av = fabsf(xb[i]);
+                    int m = fp4q_ref_e2m1_round(av * rr);
+                    float xh = fp4q_ref_e2m1_value(m) * D;
+                    best = best + elem_err(av, xh, NULL, i);
+                    nib[i] = (uint8_t)((signbit(xb[i]) ? 8 : 0) | m);
+                }
+            } else if (a == 0.0f) {
+                /* all-zero block: scale byte 0, codes keep only the sign */
+                sbyte = 0;
+                for (int i = 0; i < B; ++i)
+                    nib[i] = (uint8_t)(signbit(xb[i]) ? 8 : 0);
+                best = 0.0;
+                second = (q->format == REF_IF4 || q->rule == REF_SWEEP) ? 0.0 : INFINITY;
+            } else {
+                int sb = fp4q_ref_base_scale(xb, B, q->S);
+                if (q->format == REF_IF4) {
+                    double ef = fp4q_ref_nvfp4_block(xb, B, w, q->S, sb, nib);
+                    double ei = fp4q_ref_int4_block(xb, B, w, q->S, sb, tmp);
+                    if (ei < ef) {
+                        memcpy(nib, tmp, (size_t)B);
+                        sbyte = (uint8_t)(sb | 0x80);
+                        best = ei;
+                        second = ef;
+                    } else {
+                        sbyte = (uint8_t)sb;
+                        best = ef;
+                        second = ei;
+                    }
+                } else if (q->rule == REF_ABSMAX) {
+                    sbyte = (uint8_t)sb;
+                    best = fp4q_ref_nvfp4_block(xb, B, w, q->S, sb, nib);
+                } else {
+                    int cbest = -1;
+                    for (int k = q->lo; k <= q->hi; ++k) {
+                        int c = sb + k;
+                        if (c < 0x01 || c > 0x7E)
+                            continue;
+                        double E = fp4q_ref_nvfp4_block(xb, B, w, q->S, c, NULL);
+                        if (cbest < 0 || E < best) {
+                            if (cbest >= 0)
+                                second = best;
+                            best = E;
+                            cbest = c;
+                        } else if (E < second) {
+                            second = E;
+                        }
+                    }
+                    sbyte = (uint8_t)cbest;
+                    fp4q_ref_nvfp4_block(xb, B, w, q->S, cbest, nib);
+                }
+            }
+            put_nibbles(q->codes, e0, nib, B);
+            q->scales[bi] = sbyte;
+            if (q->best)
+                q->best[bi] = best;
+            if (q->second)
+                q->second[bi] = second;
+        }
+    }
+}
+
+typedef struct {
+    const float* xr;
+    int64_t cols;
+    float* rowmax;
+} max_ctx;
+
+static void max_rows(void* p, int64_t r0, int64_t r1)
+{
+    max_ctx* m = (max_ctx*)p;
+    for (int64_t r = r0; r < r1; ++r) {
+        float g = 0.0f;
+        const float* row = m->xr + r * m->cols;
+        for (int64_t j = 0; j < m->cols; ++j) {
+            float v = fabsf(row[j]);
+            if (v > g)
+                g = v;
+        }
+        m->rowmax[r] = g;
+    }
+}
+
+static int check_common(int format, int block, int rotate, int64_t rows, int64_t cols)
+{
+    if (rows < 0 || cols < 0)
+        return -3;
+    if (format == REF_MXFP4) {
+        if (block != 32)
+            return -4;
+    } else if (format == REF_NVFP4 || format == REF_IF4) {
+        if (block != 16)
+            return -4;
+    } else {
+        return -2;
+    }
+    if (cols % block)
+        return -3;
+    if (rotate != 0 && rotate != block)
+        return -2;
+    return 0;
+}
+
+int fp4q_ref_quantize(int format, int block, int scale_rule, int objective,
+                      int sweep_lo, int sweep_hi, int rotate,
+                      int global_scale_given,
+                      const void* x, int x_dtype, int64_t rows, int64_t cols,
+                      const float* importance,
+                      uint8_t* codes, uint8_t* scales, float* global_scale,
+                      double* best_err, double* second_err, int nthreads)
+{
+    int rc = check_common(format, block, rotate, rows, cols);
+    if (rc)
+        return rc;
+    if (!x || !codes || !scales)
+        return -1;
+    if (format != REF_MXFP4 && !global_scale)
+        return -1;
+    if (objective == REF_WMSE && !importance)
+        return -1;
+    if (scale_rule == REF_SWEEP && (format != REF_NVFP4 || sweep_lo > sweep_hi))
+        return -4;
+
+    int64_t n = rows * cols;
+    float* xr = (float*)malloc(sizeof(float) * (size_t)(n > 0 ? n : 1));
+    if (!xr)
+        return -6;
+    fp4q_ref_prepare(x, x_dtype, rows, cols, rotate, xr, nthreads);
+
+    float S = 1.0f;
+    if (format != REF_MXFP4) {
+        if (global_scale_given) {
+            S = *global_scale;
+        } else {
+            float* rowmax = (float*)calloc((size_t)(rows > 0 ? rows : 1), sizeof(float));
+            max_ctx mc = {xr, cols, rowmax};
+            parallel_rows(rows, nthreads, max_rows, &mc);
+            float g = 0.0f;
+            for (int64_t r = 0; r < rows; ++r)
+                if (rowmax[r] > g)
+                    g = rowmax[r];
+            free(rowmax);
+            S = fp4q_ref_global_scale(g);
+            *global_scale = S;
+        }
+    }
+
+    quant_ctx q = {format, block, scale_rule, objective, sweep_lo, sweep_hi,
+                   xr, cols, importance, S, codes, scales, best_err, second_err};
+    parallel_rows(rows, nthreads, quant_rows, &q);
+    free(xr);
+    return 0;
+}
+
+/* ------------------------------------------------------------------------ */
+/* dequantize                                                               */
+/* ------------------------------------------------------------------------ */
+
+typedef struct {
+    int format, block, unrotate;
+    const uint8_t* codes;
+    const uint8_t* scales;
+    float S;
+    int64_t cols;
+    float* out; /* f32 [rows, cols] */
+} deq_ctx;
+
+/* value of one stored element of block with scale byte sb */
+static float deq_elem(int format, int sb, int nibble, float S)
+{
+    if (format == REF_MXFP4) {
+        float D = fp4q_ref_e8m0_value(sb);
+        float v = fp4q_ref_e2m1_value(nibble & 7) * D;
+        return (nibble & 8) ? -v : v;
+    }
+    if (format == REF_IF4 && (sb & 0x80)) {
+        float D = fp4q_ref_e4m3_value(sb & 0x7F) * S;
+        float Di = D * fp4q_ref_int4_step();
+        int q = (nibble & 8) ? nibble - 16 : nibble;
+        return (float)q * Di;
+    }
+    int byte = (format == REF_IF4) ? (sb & 0x7F) : sb;
+    float D = fp4q_ref_e4m3_value(byte) * S;
+    float v = fp4q_ref_e2m1_value(nibble & 7) * D;
+    return (nibble & 8) ? -v : v;
+}
+
+static void deq_rows(void* p, int64_t r0, int64_t r1)
+{
+    deq_ctx* d = (deq_ctx*)p;
+    const int B = d->block;
+    const int64_t nbr = d->cols / B;
+    for (int64_t r = r0; r < r1; ++r) {
+        for (int64_t jb = 0; jb < nbr; ++jb) {
+            int64_t e0 = r * d->cols + jb * B;
+            int sb = d->scales[r * nbr + jb];
+            float* o = d->out + e0;
+            for (int i = 0; i < B; ++i) {
+                int64_t e = e0 + i;
+                int nib = (e & 1) ? (d->codes[e / 2] >> 4) : (d->codes[e / 2] & 0xF);
+                o[i] = deq_elem(d->format, sb, nib, d->S);
+            }
+            if (d->unrotate)
+                fp4q_ref_fwht(o, B);
+        }
+    }
+}
+
+static float* dequant_f32(int format, int block, const uint8_t* codes,
+                          const uint8_t* scales, float S, int64_t rows,
+                          int64_t cols, int unrotate, int nthreads)
+{
+    int64_t n = rows * cols;
+    float* out = (float*)malloc(sizeof(float) * (size_t)(n > 0 ? n : 1));
+    if (!out)
+        return NULL;
+    deq_ctx d = {format, block, unrotate, codes, scales, S, cols, out};
+    parallel_rows(rows, nthreads, deq_rows, &d);
+    return out;
+}
+
+int fp4q_ref_dequantize(int format, int block, const uint8_t* codes,
+                        const uint8_t* scales, const float* global_scale,
+                        int64_t rows, int64_t cols, int unrotate,
+                        void* y, int y_dtype, int nthreads)
+{
+    int rc = check_common(format, block, unrotate, rows, cols);
+    if (rc)
+        return rc;
+    if (!codes || !scales || !y)
+        return -1;
+    if (format != REF_MXFP4 && !global_scale)
+        return -1;
+    float S = (format == REF_MXFP4) ? 1.0f : *global_scale;
+    float* f = dequant_f32(format, block, codes, scales, S, rows, cols, unrotate, nthreads);
+    if (!f)
+        return -6;
+    int64_t n = rows * cols;
+    for (int64_t k = 0; k < n; ++k) {
+        if (y_dtype == REF_BF16)
+            ((uint16_t*)y)[k] = fp4q_ref_f32_to_bf16(f[k]);
+        else
+            ((float*)y)[k] = f[k];
+    }
+    free(f);
+    return 0;
+}
+
+/* ------------------------------------------------------------------------ */
+/* error                                                                    */
+/* ------------------------------------------------------------------------ */
+
+typedef struct {
+    const float* x;  /* widened, un-rotated */
+    const float* xh; /* dequantized, un-rotated */
+    const float* imp;
+    int64_t cols;
+    double* rs;  /* per-row sum of squared errors */
+    double* rws; /* per-row importance-weighted sum */
+} err_ctx;
+
+static void err_rows(void* p, int64_t r0, int64_t r1)
+{
+    err_ctx* e = (err_ctx*)p;
+    for (int64_t r = r0; r < r1; ++r) {
+        double s = 0.0, ws = 0.0;
+        for (int64_t j = 0; j < e->cols; ++j) {
+            int64_t k = r * e->cols + j;
+            double d = (double)e->x[k] - (double)e->xh[k];
+            double t = d * d;
+            s = s + t;
+            if (e->imp)
+                ws = ws + (double)e->imp[j] * t;
+        }
+        e->rs[r] = s;
+        e->rws[r] = ws;
+    }
+}
+
+/* MSE = sum (x - xhat)^2 / N and WMSE = sum w_col (x - xhat)^2 / N in the
+ * caller's (un-rotated) domain [SS, Method 1: objectives]. */
+int fp4q_ref_error(int format, int block, int rotate,
+                   const void* x, int x_dtype, int64_t rows, int64_t cols,
+                   const float* importance, const uint8_t* codes,
+                   const uint8_t* scales, const float* global_scale,
+                   double out[2], int nthreads)
+{
+    int rc = check_common(format, block, rotate, rows, cols);
+    if (rc)
+        return rc;
+    if (!x || !codes || !scales || !out)
+        return -1;
+    if (format != REF_MXFP4 && !global_scale)
+        return -1;
+    int64_t n = rows * cols;
+    if (n == 0) {
+        out[0] = 0.0;
+        out[1] = importance ? 0.0 : NAN;
+        return 0;
+    }
+    float S = (format == REF_MXFP4) ? 1.0f : *global_scale;
+    float* xw = (float*)malloc(sizeof(float) * (size_t)n);
+    fp4q_ref_prepare(x, x_dtype, rows, cols, 0, xw, nthreads);
+    float* xh = dequant_f32(format, block, codes, scales, S, rows, cols, rotate, nthreads);
+    double* rs = (double*)calloc((size_t)rows, sizeof(double));
+    double* rws = (double*)calloc((size_t)rows, sizeof(double));
+    err_ctx e = {xw, xh, importance, cols, rs, rws};
+    parallel_rows(rows, nthreads, err_rows, &e);
+    double s = 0.0, ws = 0.0;
+    for (int64_t r = 0; r < rows; ++r) {
+        s = s + rs[r];
+        ws = ws + rws[r];
+    }
+    out[0] = s / (double)n;
+    out[1] = importance ? ws / (double)n : NAN;
+    free(xw);
+    free(xh);
+    free(rs);
+    free(rws);
+    return 0;
+}

@@ -1,0 +1,178 @@
+"""An independent, exact, tiny-input statement of the quantizer.
+
+Used only by the tests to pin the C oracle.  It shares nothing with the
+oracle: the formats are built from their bit-field definitions with exact
+rationals, the binary32 steps of the scale computation are numpy.float32
+operations, every rounding decision is an exhaustive nearest-value search in
+exact rational arithmetic, and every error is an exact rational.  It is far
+too slow for anything but a handful of blocks.
+"""
+from fractions import Fraction as Fr
+
+import numpy as np
+
+f32 = np.float32
+
+
+def e2m1_grid():
+    """The 8 non-negative E2M1 values, by code: 2 exponent bits (bias 1),
+    1 mantissa bit, exponent field 0 subnormal."""
+    vals = []
+    for code in range(8):
+        e, m = code >> 1, code & 1
+        vals.append(Fr(m, 2) if e == 0 else (1 + Fr(m, 2)) * Fr(2) ** (e - 1))
+    return vals
+
+
+def e4m3_values():
+    """Values of E4M3FN bytes 0x00..0x7E (0x7F is NaN): 4 exponent bits with
+    bias 7, 3 mantissa bits, exponent field 0 subnormal."""
+    vals = []
+    for b in range(0x7F):
+        e, m = b >> 3, b & 7
+        vals.append(Fr(m, 8) * Fr(2) ** -6 if e == 0 else (1 + Fr(m, 8)) * Fr(2) ** (e - 7))
+    return vals
+
+
+E2M1 = e2m1_grid()
+E4M3 = e4m3_values()
+
+
+def nearest(y, grid):
+    """Index of the value of `grid` (ascending) nearest to the rational y,
+    the even index on an exact tie."""
+    best, bd = 0, None
+    for i, g in enumerate(grid):
+        d = abs(y - g)
+        if bd is None or d < bd or (d == bd and i % 2 == 0 and best % 2 == 1):
+            best, bd = i, d
+    return best
+
+
+def global_scale(g):
+    g = f32(g)
+    if g == 0:
+        return f32(1.0)
+    s = g / f32(1536.0)
+    return max(s, f32(2.0 ** -117))
+
+
+def base_byte(a, S):
+    t = f32(a) / (f32(6.0) * f32(S))
+    b = nearest(Fr(float(t)), E4M3)
+    return max(b, 1)
+
+
+def encode_fp4(xb, S, c, w=None):
+    """(exact error, nibbles) of one prepared block with scale byte c."""
+    S = f32(S)
+    D = f32(float(E4M3[c])) * S
+    r = f32(1.0) / D
+    err = Fr(0)
+    nib = []
+    for i, x in enumerate(xb):
+        x = f32(x)
+        a = abs(x)
+        y = a * r
+        m = nearest(Fr(float(y)), E2M1)
+        xh = f32(float(E2M1[m])) * D
+        e = (Fr(float(a)) - Fr(float(xh))) ** 2
+        if w is not None:
+            e *= Fr(float(f32(w[i])))
+        err += e
+        nib.append((8 if np.signbit(x) else 0) | m)
+    return err, nib
+
+
+def encode_int4(xb, S, c, w=None):
+    S = f32(S)
+    D = f32(float(E4M3[c])) * S
+    Di = D * (f32(6.0) / f32(7.0))
+    ri = f32(1.0) / Di
+    err = Fr(0)
+    nib = []
+    for i, x in enumerate(xb):
+        x = f32(x)
+        a = abs(x)
+        y = a * ri
+        q = nearest(Fr(float(y)), [Fr(k) for k in range(8)])
+        xh = f32(q) * Di
+        e = (Fr(float(a)) - Fr(float(xh))) ** 2
+        if w is not None:
+            e *= Fr(float(f32(w[i])))
+        err += e
+        nib.append((-q if np.signbit(x) else q) & 0xF)
+    return err, nib
+
+
+def quantize_block_nvfp4(xb, S, sweep=None, w=None):
+    """Returns (scale byte, nibbles, exact error, errors by candidate)."""
+    a = max(abs(f32(v)) for v in xb)
+    if a == 0:
+        return 0, [(8 if np.signbit(f32(v)) else 0) for v in xb], Fr(0), {}
+    sb = base_byte(a, S)
+    if sweep is None:
+        e, nib = encode_fp4(xb, S, sb, w)
+        return sb, nib, e, {sb: e}
+    lo, hi = sweep
+    errs = {}
+    for k in range(lo, hi + 1):
+        c = sb + k
+        if 1 <= c <= 0x7E:
+            errs[c] = encode_fp4(xb, S, c, w)[0]
+    cbest = min(errs, key=lambda c: (errs[c], c))
+    e, nib = encode_fp4(xb, S, cbest, w)
+    return cbest, nib, e, errs
+
+
+def quantize_block_if4(xb, S, w=None):
+    a = max(abs(f32(v)) for v in xb)
+    if a == 0:
+        return 0, [(8 if np.signbit(f32(v)) else 0) for v in xb], Fr(0)
+    sb = base_byte(a, S)
+    ef, nf = encode_fp4(xb, S, sb, w)
+    ei, ni = encode_int4(xb, S, sb, w)
+    if ei < ef:
+        return sb | 0x80, ni, ei
+    return sb, nf, ef
+
+
+def quantize_block_mxfp4(xb):
+    a = max(abs(f32(v)) for v in xb)
+    if a == 0:
+        e = -127
+    else:
+        # floor(log2 a) from the exact rational value
+        q = Fr(float(a))
+        e = 0
+        while q >= 2:
+            q /= 2
+            e += 1
+        while q < 1:
+            q *= 2
+            e -= 1
+        e -= 2
+    e = min(127, max(-127, e))
+    D = Fr(2) ** e
+    nib = []
+    err = Fr(0)
+    for x in xb:
+        x = f32(x)
+        av = Fr(float(abs(x)))
+        m = nearest(av / D, E2M1)
+        err += (av - E2M1[m] * D) ** 2
+        nib.append((8 if np.signbit(x) else 0) | m)
+    return e + 127, nib, err
+
+
+def hadamard(n):
+    """Sylvester Hadamard matrix (natural order), integer entries."""
+    H = np.array([[1]], dtype=np.int64)
+    while H.shape[0] < n:
+        H = np.block([[H, H], [H, -H]])
+    return H
+
+
+def pack(nibbles):
+    nib = list(nibbles)
+    return bytes((nib[i] & 0xF) | ((nib[i + 1] & 0xF) << 4) for i in range(0, len(nib), 2))
