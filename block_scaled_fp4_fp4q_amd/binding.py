@@ -1,0 +1,199 @@
+"""Thin ctypes binding of libfp4q.so (include/fp4q.h).
+
+Argument marshalling only: tensors are torch tensors on a ROCm device, whose
+data pointers and current HIP stream are handed to the C ABI unchanged.  All
+arithmetic happens in the library's HIP kernels.  There is no fallback: if the
+library is missing, or a call is rejected, this module raises.
+"""
+import ctypes as C
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libfp4q.so")
+
+FP4Q_NVFP4, FP4Q_MXFP4, FP4Q_IF4 = 0, 1, 2
+FP4Q_F32, FP4Q_BF16 = 0, 1
+FP4Q_SCALE_ABSMAX, FP4Q_SCALE_SWEEP = 0, 1
+FP4Q_OBJ_MSE, FP4Q_OBJ_WMSE = 0, 1
+
+STATUS = {0: "FP4Q_OK", -1: "FP4Q_E_NULL", -2: "FP4Q_E_ARG", -3: "FP4Q_E_SHAPE",
+          -4: "FP4Q_E_UNSUPPORTED", -5: "FP4Q_E_HIP", -6: "FP4Q_E_ALIGN"}
+
+# every symbol include/fp4q.h declares
+EXPORTS = ("fp4q_workspace_bytes", "fp4q_quantize", "fp4q_dequantize", "fp4q_error",
+           "fp4q_status_string", "fp4q_abi_version")
+
+
+class fp4q_spec(C.Structure):
+    _fields_ = [("format", C.c_int32), ("block", C.c_int32), ("scale_rule", C.c_int32),
+                ("objective", C.c_int32), ("sweep_lo", C.c_int32), ("sweep_hi", C.c_int32),
+                ("rotate", C.c_int32), ("global_scale_given", C.c_int32)]
+
+
+class Fp4qError(RuntimeError):
+    def __init__(self, fn, status):
+        self.status = status
+        msg = _lib_handle().fp4q_status_string(status).decode() if _LIB is not None else ""
+        super().__init__(f"{fn} returned {STATUS.get(status, status)}: {msg}")
+
+
+_LIB = None
+
+
+def _lib_handle():
+    global _LIB
+    if _LIB is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is not built; run __graft_entry__.build() "
+                              "or python block_scaled_fp4_fp4q_amd/build.py")
+        L = C.CDLL(LIB_PATH)
+        vp, i32, i64, sz = C.c_void_p, C.c_int32, C.c_int64, C.c_size_t
+        sp = C.POINTER(fp4q_spec)
+        L.fp4q_workspace_bytes.restype = sz
+        L.fp4q_workspace_bytes.argtypes = [sp, i64, i64]
+        L.fp4q_quantize.restype = C.c_int
+        L.fp4q_quantize.argtypes = [sp, vp, i32, i64, i64, vp, vp, vp, vp, vp, sz, vp]
+        L.fp4q_dequantize.restype = C.c_int
+        L.fp4q_dequantize.argtypes = [sp, vp, vp, vp, i64, i64, i32, vp, i32, vp]
+        L.fp4q_error.restype = C.c_int
+        L.fp4q_error.argtypes = [sp, vp, i32, i64, i64, vp, vp, vp, vp, vp, sz,
+                                 C.POINTER(C.c_double), vp]
+        L.fp4q_status_string.restype = C.c_char_p
+        L.fp4q_status_string.argtypes = [C.c_int]
+        L.fp4q_abi_version.restype = C.c_int
+        L.fp4q_abi_version.argtypes = []
+        _LIB = L
+    return _LIB
+
+
+def lib():
+    return _lib_handle()
+
+
+# ---------------------------------------------------------------------------
+# marshalling helpers
+# ---------------------------------------------------------------------------
+
+def _ptr(t):
+    return None if t is None else C.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return C.c_void_p(stream.cuda_stream)
+
+
+def _dtype_code(t):
+    if t.dtype == torch.float32:
+        return FP4Q_F32
+    if t.dtype == torch.bfloat16:
+        return FP4Q_BF16
+    raise TypeError(f"unsupported dtype {t.dtype}; use float32 or bfloat16")
+
+
+def _check(fn, st):
+    if st != 0:
+        raise Fp4qError(fn, st)
+
+
+def make_spec(format=FP4Q_NVFP4, scale_rule=FP4Q_SCALE_ABSMAX, objective=FP4Q_OBJ_MSE,
+              window=None, rotate=0, global_scale_given=False):
+    block = 32 if format == FP4Q_MXFP4 else 16
+    lo, hi = window if window is not None else ((-8, 7) if objective == FP4Q_OBJ_WMSE else (-3, 7))
+    return fp4q_spec(format, block, scale_rule, objective, lo, hi, rotate, int(global_scale_given))
+
+
+def _as_2d(x):
+    if x.dim() < 2:
+        raise ValueError("x must have at least 2 dimensions (rows, cols)")
+    if not x.is_contiguous():
+        raise ValueError("x must be contiguous")
+    return x.reshape(-1, x.shape[-1])
+
+
+# ---------------------------------------------------------------------------
+# the C ABI, one Python function per entry point
+# ---------------------------------------------------------------------------
+
+def fp4q_workspace_bytes(spec, rows, cols):
+    return int(_lib_handle().fp4q_workspace_bytes(C.byref(spec), rows, cols))
+
+
+def fp4q_quantize(spec, x, importance, codes, scales, global_scale, workspace, stream=None):
+    x2 = _as_2d(x)
+    rows, cols = x2.shape
+    st = _lib_handle().fp4q_quantize(C.byref(spec), _ptr(x2), _dtype_code(x2), rows, cols,
+                                     _ptr(importance), _ptr(codes), _ptr(scales),
+                                     _ptr(global_scale), _ptr(workspace), workspace.numel(),
+                                     _stream(stream))
+    _check("fp4q_quantize", st)
+
+
+def fp4q_dequantize(spec, codes, scales, global_scale, rows, cols, unrotate, y, stream=None):
+    st = _lib_handle().fp4q_dequantize(C.byref(spec), _ptr(codes), _ptr(scales),
+                                       _ptr(global_scale), rows, cols, unrotate, _ptr(y),
+                                       _dtype_code(y), _stream(stream))
+    _check("fp4q_dequantize", st)
+
+
+def fp4q_error(spec, x, importance, codes, scales, global_scale, workspace, stream=None):
+    x2 = _as_2d(x)
+    rows, cols = x2.shape
+    out = (C.c_double * 2)()
+    st = _lib_handle().fp4q_error(C.byref(spec), _ptr(x2), _dtype_code(x2), rows, cols,
+                                  _ptr(importance), _ptr(codes), _ptr(scales),
+                                  _ptr(global_scale), _ptr(workspace), workspace.numel(),
+                                  out, _stream(stream))
+    _check("fp4q_error", st)
+    return out[0], out[1]
+
+
+# ---------------------------------------------------------------------------
+# convenience: allocate outputs with torch, then call the entry points
+# ---------------------------------------------------------------------------
+
+def alloc_workspace(spec, rows, cols, device):
+    n = fp4q_workspace_bytes(spec, rows, cols)
+    if n == 0:
+        raise ValueError("invalid spec or shape")
+    return torch.empty(n, dtype=torch.uint8, device=device)
+
+
+def quantize(x, format=FP4Q_NVFP4, scale_rule=FP4Q_SCALE_ABSMAX, objective=FP4Q_OBJ_MSE,
+             window=None, rotate=0, importance=None, global_scale=None, workspace=None,
+             stream=None):
+    """Returns (codes uint8 [rows*cols/2], scales uint8 [rows*cols/block],
+    global_scale float32 [1])."""
+    spec = make_spec(format, scale_rule, objective, window, rotate, global_scale is not None)
+    x2 = _as_2d(x)
+    rows, cols = x2.shape
+    dev = x.device
+    codes = torch.empty(rows * cols // 2, dtype=torch.uint8, device=dev)
+    scales = torch.empty(rows * cols // spec.block, dtype=torch.uint8, device=dev)
+    if global_scale is None:
+        gs = torch.empty(1, dtype=torch.float32, device=dev)
+    else:
+        gs = torch.as_tensor(global_scale, dtype=torch.float32, device=dev).reshape(1).clone()
+    ws = workspace if workspace is not None else alloc_workspace(spec, rows, cols, dev)
+    fp4q_quantize(spec, x2, importance, codes, scales, gs, ws, stream)
+    return codes, scales, gs
+
+
+def dequantize(codes, scales, global_scale, rows, cols, format=FP4Q_NVFP4, unrotate=0,
+               dtype=torch.float32, stream=None):
+    spec = make_spec(format)
+    y = torch.empty(rows, cols, dtype=dtype, device=codes.device)
+    fp4q_dequantize(spec, codes, scales, global_scale, rows, cols, unrotate, y, stream)
+    return y
+
+
+def error(x, codes, scales, global_scale, format=FP4Q_NVFP4, rotate=0, importance=None,
+          workspace=None, stream=None):
+    spec = make_spec(format, rotate=rotate)
+    x2 = _as_2d(x)
+    rows, cols = x2.shape
+    ws = workspace if workspace is not None else alloc_workspace(spec, rows, cols, x.device)
+    return fp4q_error(spec, x2, importance, codes, scales, global_scale, ws, stream)

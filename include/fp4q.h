@@ -1,0 +1,159 @@
+/*
+ * fp4q.h -- C ABI of libfp4q.so: block-scaled 4-bit (FP4) quantization of a
+ * tensor with error-minimizing scale selection, for AMD Instinct MI355X
+ * (gfx950).
+ *
+ * Formats (see the pages cited at each entry point):
+ *   NVFP4  E2M1 element codes, 16-element blocks, one E4M3 scale byte per
+ *          block under one fp32 global scale S.
+ *   MXFP4  E2M1 element codes, 32-element blocks, one E8M0 (power-of-two)
+ *          scale byte per block, no global scale.
+ *   IF4    NVFP4 layout; each block holds either FP4 (E2M1) codes or scaled
+ *          INT4 codes, and bit 7 (the sign bit) of its E4M3 scale byte says
+ *          which: 0 = FP4, 1 = INT4.
+ *
+ * Tensor layout.  x is a row-major [rows, cols] tensor; blocks are `block`
+ * consecutive elements of one row (cols % block == 0), numbered in memory
+ * order.  A KV cache [B, H, T, D] is passed as [B*H*T, D].
+ *   codes   [rows*cols/2] bytes: element 2k in the low nibble of byte k,
+ *           element 2k+1 in the high nibble.  An FP4 nibble is
+ *           (sign << 3) | magnitude code, magnitudes 0..7 =
+ *           {0, 0.5, 1, 1.5, 2, 3, 4, 6}; an INT4 nibble is the 4-bit two's
+ *           complement of the integer in [-7, 7].
+ *   scales  [rows*cols/block] bytes, one per block in memory order.
+ *   S       one fp32 (NVFP4 and IF4 only).
+ *
+ * Ownership and threading.  Every tensor pointer is a DEVICE pointer owned by
+ * the caller, as is the workspace; the library allocates nothing, frees
+ * nothing and keeps no state between calls.  Calls are asynchronous on the
+ * given stream (a hipStream_t passed as void*; NULL is the null stream)
+ * except fp4q_error, which waits for its own result.  Two calls may run
+ * concurrently only with separate workspaces.
+ *
+ * Errors.  Every entry point returns an fp4q_status.  Argument, shape and
+ * alignment errors are detected on the host before anything is launched and
+ * leave every output untouched.  A failed launch returns FP4Q_E_HIP.  Faults
+ * inside a kernel surface at the caller's next synchronization.
+ *
+ * An empty tensor (rows == 0 or cols == 0) is valid; its tensor pointers may
+ * then be NULL, and a computed global scale is 1.
+ *
+ * Preconditions (not checked, results unspecified otherwise): inputs are
+ * finite; a caller-supplied global scale is a normal fp32 in
+ * [2^-117, 2^119]; output buffers do not overlap inputs.
+ */
+#ifndef FP4Q_H
+#define FP4Q_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define FP4Q_ABI_VERSION 1
+
+typedef enum {
+    FP4Q_OK = 0,
+    FP4Q_E_NULL = -1,        /* a required pointer is NULL                   */
+    FP4Q_E_ARG = -2,         /* bad enum, window, rotation or workspace size */
+    FP4Q_E_SHAPE = -3,       /* negative sizes or cols % block != 0          */
+    FP4Q_E_UNSUPPORTED = -4, /* a valid combination this library lacks       */
+    FP4Q_E_HIP = -5,         /* the HIP runtime refused a launch or copy     */
+    FP4Q_E_ALIGN = -6        /* a tensor pointer is not aligned as required  */
+} fp4q_status;
+
+typedef enum { FP4Q_NVFP4 = 0, FP4Q_MXFP4 = 1, FP4Q_IF4 = 2 } fp4q_format;
+typedef enum { FP4Q_F32 = 0, FP4Q_BF16 = 1 } fp4q_dtype;
+typedef enum { FP4Q_SCALE_ABSMAX = 0, FP4Q_SCALE_SWEEP = 1 } fp4q_scale_rule;
+typedef enum { FP4Q_OBJ_MSE = 0, FP4Q_OBJ_WMSE = 1 } fp4q_objective;
+
+/* The problem statement of one quantization.
+ *   format      fp4q_format.
+ *   block       16 for NVFP4 and IF4, 32 for MXFP4.
+ *   scale_rule  ABSMAX: the block scale is the block maximum mapped onto the
+ *               FP4 maximum 6 and rounded to FP8 ("AbsMax", ScaleSweep page,
+ *               Problem definition).  SWEEP: ScaleSweep -- every E4M3 bit
+ *               pattern s_base + k, k in [sweep_lo, sweep_hi], is tried and
+ *               the one of least block error kept (ScaleSweep page, Method 2
+ *               and 3).  SWEEP is NVFP4-only.
+ *   objective   MSE, or WMSE weighted by a per-column importance vector
+ *               (ScaleSweep page, Method 1).  Used by SWEEP and by IF4's
+ *               FP4-vs-INT4 pick.
+ *   sweep_lo, sweep_hi
+ *               the window of bit-pattern offsets, -126 <= lo <= hi <= 126;
+ *               the pages use [-3, 7] for MSE and [-8, 7] for WMSE.
+ *               Patterns outside [0x01, 0x7E] are skipped.
+ *   rotate      0, or equal to block: apply the orthonormal Sylvester block
+ *               Hadamard transform to every block before quantizing
+ *               ("Bridging the Gap ... Microscaling FP4" page, Method 1).
+ *   global_scale_given
+ *               0: S = max|x| / (256*6) is computed on the device (ScaleSweep
+ *               page, Method 2) and written to *global_scale; 1: *global_scale
+ *               is read as S.  Ignored for MXFP4. */
+typedef struct {
+    int32_t format;
+    int32_t block;
+    int32_t scale_rule;
+    int32_t objective;
+    int32_t sweep_lo;
+    int32_t sweep_hi;
+    int32_t rotate;
+    int32_t global_scale_given;
+} fp4q_spec;
+
+/* Bytes of device workspace that fp4q_quantize and fp4q_error need for this
+ * problem (at least 256; the workspace must be 256-byte aligned).  Returns 0
+ * for an invalid spec. */
+size_t fp4q_workspace_bytes(const fp4q_spec* spec, int64_t rows, int64_t cols);
+
+/* Quantize x [rows, cols] (dtype FP4Q_F32 or FP4Q_BF16; 16-byte aligned).
+ *   importance  fp32 [cols] per-input-column weights, required for WMSE,
+ *               ignored otherwise (may be NULL).
+ *   codes       [rows*cols/2] bytes, 8-byte aligned (16 for MXFP4).
+ *   scales      [rows*cols/block] bytes.
+ *   global_scale  one fp32: output (or input when global_scale_given); may be
+ *               NULL for MXFP4.
+ *   workspace   device scratch of fp4q_workspace_bytes() bytes.
+ * Per block (ScaleSweep page, Method; Adaptive Block-Scaled Data Types page,
+ * Methodology): the block maximum a gives the base scale
+ * s_base = E4M3(a / (6 S)) (at least 0x01; an all-zero block gets scale 0 and
+ * sign-only codes); each element is encoded as the nearest E2M1 value of
+ * |x| * fl32(1 / fl32(s S)) (ties to the even code, saturating at 6).  IF4
+ * also encodes the block as integers q = round(|x| / (D 6/7)) clamped to 7
+ * and keeps INT4 only when its error is strictly lower.  MXFP4 uses the
+ * power of two 2^(floor(log2 a) - 2). */
+fp4q_status fp4q_quantize(const fp4q_spec* spec, const void* x, int32_t x_dtype,
+                          int64_t rows, int64_t cols, const float* importance,
+                          uint8_t* codes, uint8_t* scales, float* global_scale,
+                          void* workspace, size_t ws_bytes, void* stream);
+
+/* Dequantize codes/scales/S into y [rows, cols] (y_dtype FP4Q_F32 or
+ * FP4Q_BF16, 16-byte aligned): x_hat = +-value(code) * D, D = fl32(s S) for
+ * NVFP4/IF4 (fl32(D * fl32(6/7)) for IF4 INT4 blocks, the 6/7 method) or
+ * 2^(byte-127) for MXFP4; unrotate (0 or block) applies the block Hadamard,
+ * which is its own inverse.  bf16 output is rounded to nearest even. */
+fp4q_status fp4q_dequantize(const fp4q_spec* spec, const uint8_t* codes,
+                            const uint8_t* scales, const float* global_scale,
+                            int64_t rows, int64_t cols, int32_t unrotate,
+                            void* y, int32_t y_dtype, void* stream);
+
+/* Reconstruction error in the caller's (un-rotated) domain:
+ * out_host[0] = sum (x - x_hat)^2 / N, out_host[1] = sum w_col (x - x_hat)^2
+ * / N (NaN when importance is NULL), accumulated in fp64 (ScaleSweep page,
+ * Method 1: MSE and WMSE).  x_hat is the dequantized tensor, un-rotated when
+ * spec->rotate is set.  Blocks until the two doubles are on the host. */
+fp4q_status fp4q_error(const fp4q_spec* spec, const void* x, int32_t x_dtype,
+                       int64_t rows, int64_t cols, const float* importance,
+                       const uint8_t* codes, const uint8_t* scales,
+                       const float* global_scale, void* workspace, size_t ws_bytes,
+                       double out_host[2], void* stream);
+
+const char* fp4q_status_string(fp4q_status status);
+int fp4q_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* FP4Q_H */

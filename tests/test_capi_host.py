@@ -1,0 +1,125 @@
+"""The C ABI on the host: the library loads, exports every symbol the header
+declares, and rejects bad arguments before any HIP call (no GPU needed)."""
+import ctypes as C
+import os
+import re
+
+import pytest
+
+from block_scaled_fp4_fp4q_amd import binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fp4q.h")
+
+# fake, suitably aligned device addresses: validation fails before any is used
+X, CODES, SCALES, GS, WS, IMP = (C.c_void_p(0x10000 * k) for k in range(1, 7))
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(B.LIB_PATH):
+        pytest.skip("libfp4q.so not built")
+    return B.lib()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(fp4q_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_binding_exports():
+    assert declared_functions() == sorted(B.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol(L):
+    for name in declared_functions():
+        assert hasattr(L, name), name
+
+
+def test_abi_version_and_status_strings(L):
+    assert L.fp4q_abi_version() == 1
+    for st in B.STATUS:
+        assert L.fp4q_status_string(st)
+    assert L.fp4q_status_string(-99) == b"unknown status"
+
+
+def spec(**kw):
+    s = B.make_spec()
+    for k, v in kw.items():
+        setattr(s, k, v)
+    return s
+
+
+def q(L, s, x=X, dtype=B.FP4Q_BF16, rows=4, cols=64, imp=None, codes=CODES, scales=SCALES,
+      gs=GS, ws=WS, ws_bytes=1 << 20):
+    return L.fp4q_quantize(C.byref(s) if s is not None else None, x, dtype, rows, cols, imp,
+                           codes, scales, gs, ws, ws_bytes, None)
+
+
+def test_workspace_bytes(L):
+    assert L.fp4q_workspace_bytes(C.byref(spec()), 4, 64) >= 256
+    assert L.fp4q_workspace_bytes(C.byref(spec()), 4, 63) == 0
+    assert L.fp4q_workspace_bytes(C.byref(spec(block=32)), 4, 64) == 0
+    assert L.fp4q_workspace_bytes(None, 4, 64) == 0
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(format=7), -2),
+    (dict(block=32), -4),
+    (dict(format=B.FP4Q_MXFP4), -4),                                  # block stays 16
+    (dict(rotate=8), -2),
+    (dict(scale_rule=5), -2),
+    (dict(objective=3), -2),
+    (dict(global_scale_given=2), -2),
+    (dict(scale_rule=B.FP4Q_SCALE_SWEEP, sweep_lo=3, sweep_hi=2), -2),
+    (dict(scale_rule=B.FP4Q_SCALE_SWEEP, sweep_lo=-127), -2),
+    (dict(scale_rule=B.FP4Q_SCALE_SWEEP, sweep_hi=127), -2),
+    (dict(scale_rule=B.FP4Q_SCALE_SWEEP, format=B.FP4Q_IF4), -4),
+])
+def test_quantize_rejects_bad_spec(L, kw, status):
+    assert q(L, spec(**kw)) == status
+
+
+def test_quantize_rejects_bad_arguments(L):
+    assert q(L, None) == -1
+    assert q(L, spec(), x=None) == -1
+    assert q(L, spec(), codes=None) == -1
+    assert q(L, spec(), scales=None) == -1
+    assert q(L, spec(), gs=None) == -1                                   # NVFP4 needs S
+    assert q(L, spec(), ws=None) == -1
+    w = spec(scale_rule=B.FP4Q_SCALE_SWEEP, objective=B.FP4Q_OBJ_WMSE)
+    assert q(L, w, imp=None) == -1                                       # WMSE needs importance
+    assert q(L, spec(), dtype=5) == -2
+    assert q(L, spec(), cols=63) == -3
+    assert q(L, spec(), rows=-1) == -3
+    assert q(L, spec(), ws_bytes=100) == -2
+    assert q(L, spec(), x=C.c_void_p(0x10008)) == -6                    # x not 16-aligned
+    assert q(L, spec(), codes=C.c_void_p(0x10004)) == -6
+    assert q(L, spec(), ws=C.c_void_p(0x10080)) == -6
+    assert q(L, w, imp=C.c_void_p(0x10004)) == -6
+
+
+def test_dequantize_and_error_reject_bad_arguments(L):
+    s = spec()
+    f = L.fp4q_dequantize
+    assert f(None, CODES, SCALES, GS, 4, 64, 0, X, 0, None) == -1
+    assert f(C.byref(s), None, SCALES, GS, 4, 64, 0, X, 0, None) == -1
+    assert f(C.byref(s), CODES, SCALES, None, 4, 64, 0, X, 0, None) == -1
+    assert f(C.byref(s), CODES, SCALES, GS, 4, 64, 3, X, 0, None) == -2
+    assert f(C.byref(s), CODES, SCALES, GS, 4, 64, 0, X, 9, None) == -2
+    assert f(C.byref(s), CODES, SCALES, GS, 4, 60, 0, X, 0, None) == -3
+    assert f(C.byref(s), CODES, SCALES, GS, 4, 64, 0, C.c_void_p(0x10004), 0, None) == -6
+    out = (C.c_double * 2)()
+    e = L.fp4q_error
+    assert e(C.byref(s), X, 1, 4, 64, None, CODES, SCALES, GS, WS, 1 << 20, None, None) == -1
+    assert e(C.byref(s), X, 1, 4, 64, None, CODES, SCALES, GS, WS, 10, out, None) == -2
+    assert e(C.byref(s), X, 1, 4, 60, None, CODES, SCALES, GS, WS, 1 << 20, out, None) == -3
+    assert e(C.byref(s), X, 4, 4, 64, None, CODES, SCALES, GS, WS, 1 << 20, out, None) == -2
+
+
+def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(B, "LIB_PATH", str(tmp_path / "missing.so"))
+    monkeypatch.setattr(B, "_LIB", None)
+    with pytest.raises(ImportError):
+        B.lib()

@@ -1,0 +1,178 @@
+"""GPU parity: the HIP library (through the C ABI) against the CPU oracle,
+element by element, for every format / rule / objective / dtype / rotation,
+at sizes that span many workgroups and end on a ragged tail, plus edge cases.
+
+Bar: codes, scale bytes, IF4 indicators, the global scale and dequantized
+values are bit-exact; the MSE/WMSE report agrees to 1e-10 relative (both
+sides accumulate binary64, only the summation order differs)."""
+import numpy as np
+import pytest
+import torch
+
+from block_scaled_fp4_fp4q_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+
+@pytest.fixture(scope="module")
+def B():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from block_scaled_fp4_fp4q_amd import binding
+    binding.lib()
+    return binding
+
+
+def to_dev(x):
+    if x.dtype == np.uint16:
+        return torch.from_numpy(x.view(np.int16).copy()).view(torch.bfloat16).to(DEV)
+    return torch.from_numpy(np.ascontiguousarray(x)).to(DEV)
+
+
+def host_bf16_bits(t):
+    return t.view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+FMT = {"nvfp4": (0, 0), "mxfp4": (1, 1), "if4": (2, 2)}  # binding code, oracle code
+
+
+def inputs(kind, rows, cols, seed):
+    if kind == "bf16":
+        x = synth.f32_to_bf16_bits((np.random.default_rng(seed).standard_t(4, (rows, cols)) * 0.02)
+                                   .astype(np.float32))
+    else:
+        x = synth.c1(rows=rows, cols=cols, seed=seed)
+    imp = np.random.default_rng(seed + 1).lognormal(0, 1, cols).astype(np.float32)
+    return x, imp
+
+
+def run_case(B, ref, fmt, rule, objective, rotate, x, imp, window=None, given=None):
+    bfmt, ofmt = FMT[fmt]
+    rows, cols = x.shape
+    xd = to_dev(x)
+    impd = to_dev(imp) if imp is not None else None
+    codes, scales, gs = B.quantize(xd, format=bfmt, scale_rule=rule, objective=objective,
+                                   window=window, rotate=rotate,
+                                   importance=impd if objective == 1 else None,
+                                   global_scale=given)
+    torch.cuda.synchronize()
+    want = ref.quantize(x, fmt=ofmt, rule=rule, objective=objective, window=window,
+                        rotate=rotate, importance=imp if objective == 1 else None,
+                        global_scale=given)
+    got_scales = scales.cpu().numpy()
+    got_codes = codes.cpu().numpy()
+    if fmt != "mxfp4":
+        assert gs.cpu().numpy()[0] == np.float32(want["S"])
+    bad = np.nonzero(got_scales != want["scales"])[0]
+    assert bad.size == 0, f"{bad.size} scale mismatches, first block {bad[:5]}"
+    assert np.array_equal(got_codes, want["codes"])
+    return xd, codes, scales, gs, want
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("rotate", [0, 16])
+@pytest.mark.parametrize("mode", ["absmax", "sweep_mse", "sweep_wmse"])
+def test_nvfp4_parity(B, ref, dtype, rotate, mode):
+    rule, obj = {"absmax": (0, 0), "sweep_mse": (1, 0), "sweep_wmse": (1, 1)}[mode]
+    seed = 10 * ["absmax", "sweep_mse", "sweep_wmse"].index(mode) + rotate + (dtype == "bf16")
+    x, imp = inputs(dtype, 37, 528, seed=seed)  # 1221 blocks: 5 workgroups, ragged tail
+    run_case(B, ref, "nvfp4", rule, obj, rotate, x, imp)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("rotate", [0, 16])
+@pytest.mark.parametrize("objective", [0, 1])
+def test_if4_parity(B, ref, dtype, rotate, objective):
+    if dtype == "bf16":
+        x = synth.c4(rows=41, cols=336, seed=rotate + objective)[0]
+    else:
+        x = synth.bf16_bits_to_f32(synth.c4(rows=41, cols=336, seed=5 + rotate)[0])
+    imp = np.random.default_rng(3).lognormal(0, 1, 336).astype(np.float32)
+    run_case(B, ref, "if4", 0, objective, rotate, x, imp)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("rotate", [0, 32])
+def test_mxfp4_parity(B, ref, dtype, rotate):
+    x = synth.c3(rows=53, cols=352, seed=rotate + 1, n_outlier_channels=3)
+    if dtype == "f32":
+        x = synth.bf16_bits_to_f32(x)
+    run_case(B, ref, "mxfp4", 0, 0, rotate, x, None)
+
+
+@pytest.mark.parametrize("window", [(0, 0), (-126, 126), (-8, 7), (2, 5)])
+def test_sweep_windows(B, ref, window):
+    x, imp = inputs("bf16", 9, 256, seed=7)
+    run_case(B, ref, "nvfp4", 1, 0, 0, x, imp, window=window)
+
+
+def test_given_global_scale(B, ref):
+    x, imp = inputs("f32", 12, 256, seed=8)
+    run_case(B, ref, "nvfp4", 1, 1, 0, x, imp, given=0.0625)
+    run_case(B, ref, "if4", 0, 0, 16, x, imp, given=0.01)
+
+
+def test_edge_blocks(B, ref):
+    # zeros, signed zeros, tiny blocks (subnormal and clamped E4M3 scales),
+    # exact midpoints, one spike, and the block holding the maximum
+    import exactspec  # noqa: F401  (tests/ is on sys.path)
+    from test_oracle_spec import adversarial_nvfp4
+    x = adversarial_nvfp4().reshape(-1, 64)
+    for fmt, rule in [("nvfp4", 0), ("nvfp4", 1), ("if4", 0), ("mxfp4", 0)]:
+        for rot in (0, 32 if fmt == "mxfp4" else 16):
+            run_case(B, ref, fmt, rule, 0, rot, x, None)
+
+
+def test_empty_and_single_block(B, ref):
+    x = np.zeros((0, 64), np.float32)
+    codes, scales, gs = B.quantize(to_dev(x))
+    torch.cuda.synchronize()
+    assert codes.numel() == 0 and gs.cpu().item() == 1.0
+    x1 = np.linspace(-3, 5, 16, dtype=np.float32).reshape(1, 16)
+    run_case(B, ref, "nvfp4", 1, 0, 16, x1, None)
+    x0 = np.zeros((3, 16), np.float32)
+    _, _, _, gs, _ = run_case(B, ref, "nvfp4", 1, 0, 0, x0, None)
+    assert gs.cpu().item() == 1.0
+
+
+@pytest.mark.parametrize("fmt,rot", [("nvfp4", 0), ("nvfp4", 16), ("if4", 0), ("if4", 16),
+                                     ("mxfp4", 0), ("mxfp4", 32)])
+def test_dequantize_and_error_parity(B, ref, fmt, rot):
+    bfmt, ofmt = FMT[fmt]
+    if fmt == "mxfp4":
+        x = synth.c3(rows=19, cols=320, seed=2, n_outlier_channels=2)
+    elif fmt == "if4":
+        x = synth.c4(rows=19, cols=320, seed=2)[0]
+    else:
+        x = synth.c2(rows=19, cols=320, seed=2)[0]
+    imp = np.random.default_rng(1).lognormal(0, 1, 320).astype(np.float32)
+    xd, codes, scales, gs, want = run_case(B, ref, fmt, 0, 0, rot, x, None)
+    rows, cols = x.shape
+    S = None if fmt == "mxfp4" else want["S"]
+    for dt, odt in [(torch.float32, 0), (torch.bfloat16, 1)]:
+        y = B.dequantize(codes, scales, gs, rows, cols, format=bfmt, unrotate=rot, dtype=dt)
+        torch.cuda.synchronize()
+        yw = ref.dequantize(want["codes"], want["scales"], S, rows, cols, fmt=ofmt,
+                            unrotate=rot, out_dtype=odt)
+        if dt == torch.float32:
+            assert np.array_equal(y.cpu().numpy().view(np.uint32), yw.view(np.uint32))
+        else:
+            assert np.array_equal(host_bf16_bits(y), yw)
+    got = B.error(xd, codes, scales, gs, format=bfmt, rotate=rot, importance=to_dev(imp))
+    exp = ref.error(x, want["codes"], want["scales"], S, fmt=ofmt, rotate=rot, importance=imp)
+    assert abs(got[0] - exp[0]) <= 1e-10 * exp[0]
+    assert abs(got[1] - exp[1]) <= 1e-10 * exp[1]
+    got = B.error(xd, codes, scales, gs, format=bfmt, rotate=rot)
+    assert np.isnan(got[1])
+
+
+def test_deterministic(B):
+    x, imp = inputs("bf16", 64, 1024, seed=3)
+    xd, impd = to_dev(x), to_dev(imp)
+    a = B.quantize(xd, scale_rule=1, objective=1, importance=impd)
+    b = B.quantize(xd, scale_rule=1, objective=1, importance=impd)
+    torch.cuda.synchronize()
+    for u, v in zip(a, b):
+        assert torch.equal(u, v)
