@@ -33,7 +33,9 @@
  * written below (D = s*S, r = 1/D, y = |x|*r); block errors are evaluated in
  * binary64, and exact ties keep the smaller scale byte (the FP4 branch for
  * IF4); the sweep offset is added to the 7-bit E4M3 magnitude pattern and
- * patterns outside [0x01, 0x7E] are skipped; S = 1 for an all-zero tensor
+ * a pattern outside [0x01, 0x7E] stands for the nearer end pattern (so a
+ * window reaching past an end adds nothing new, and a window lying wholly
+ * outside still has a candidate); S = 1 for an all-zero tensor
  * and S is never below 2^-117 so that every candidate reciprocal is finite;
  * the MXFP4 exponent is floor(log2 max|x|) - 2 clamped to [-127, 127]; the
  * Hadamard is the Sylvester (natural-order) matrix evaluated by butterflies
@@ -518,11 +520,15 @@ static void quant_rows(void* p, int64_t r0, int64_t r1)
                     sbyte = (uint8_t)sb;
                     best = fp4q_ref_nvfp4_block(xb, B, w, q->S, sb, nib);
                 } else {
-                    int cbest = -1;
+                    int cbest = -1, cprev = -1;
                     for (int k = q->lo; k <= q->hi; ++k) {
+                        /* patterns past either end of [0x01, 0x7E] stand for the
+                         * end pattern itself; each pattern is tried once */
                         int c = sb + k;
-                        if (c < 0x01 || c > 0x7E)
+                        c = c < 0x01 ? 0x01 : (c > 0x7E ? 0x7E : c);
+                        if (c == cprev)
                             continue;
+                        cprev = c;
                         double E = fp4q_ref_nvfp4_block(xb, B, w, q->S, c, NULL);
                         if (cbest < 0 || E < best) {
                             if (cbest >= 0)

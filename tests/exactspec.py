@@ -117,8 +117,8 @@ def quantize_block_nvfp4(xb, S, sweep=None, w=None):
     lo, hi = sweep
     errs = {}
     for k in range(lo, hi + 1):
-        c = sb + k
-        if 1 <= c <= 0x7E:
+        c = min(0x7E, max(0x01, sb + k))
+        if c not in errs:
             errs[c] = encode_fp4(xb, S, c, w)[0]
     cbest = min(errs, key=lambda c: (errs[c], c))
     e, nib = encode_fp4(xb, S, cbest, w)

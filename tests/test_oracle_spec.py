@@ -127,6 +127,19 @@ def test_given_global_scale_is_used(ref):
         assert list(ref.unpack_nibbles(out["codes"])[b * 16:(b + 1) * 16]) == nb
 
 
+@pytest.mark.parametrize("window", [(3, 9), (-20, -10), (-126, 126), (0, 0)])
+def test_windows_past_the_pattern_range(ref, window):
+    # a window reaching past 0x01 or 0x7E tries the end pattern; one lying
+    # wholly outside the range still yields a candidate
+    x = np.array([[1536.0] + [0.3] * 15, [1e-6] * 16, list(np.linspace(-2, 3, 16))], np.float32)
+    out = ref.quantize(x, rule=ref.SWEEP, window=window, errors=True)
+    S = X.global_scale(np.abs(x).max())
+    for b, xb in enumerate(blocks_of(x, 16)):
+        sc, nb, e, _ = X.quantize_block_nvfp4(xb, S, window)
+        assert out["scales"][b] == sc and 1 <= sc <= 0x7E
+        assert list(ref.unpack_nibbles(out["codes"])[b * 16:(b + 1) * 16]) == nb
+
+
 def test_importance_is_indexed_by_column(ref):
     # [out, in] weights: the importance weight of an element is that of its
     # input column, whatever the row (ScaleSweep page, Method 1: WMSE).
