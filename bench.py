@@ -1,0 +1,243 @@
+"""Benchmark of the block-scaled FP4 quantizer on one MI355X.
+
+One step = one fp4q_quantize call on the headline workload: NVFP4 ScaleSweep
+with importance-weighted MSE (offsets [-8, 7]) of a bf16 14336x4096 weight
+matrix (Student-t(4) * 0.02, lognormal(0,1) per-column importance), global
+scale computed on the device -- global max pass, scale finalize, sweep
+quantize.  Inputs are resident in HBM before timing starts; the step cycles
+through several input copies so that no step reads data a previous step left
+in the 256 MB Infinity Cache.
+
+Printed: one JSON line (rank 0).  `value` is quantized Gelem/s of the whole
+call; `roofline` is the dominant kernel (the sweep quantizer) timed alone
+with HIP events on the stream it runs on, against the 8 TB/s HBM peak;
+`cpu_baseline` is the CPU oracle on a bounded row sample of the same
+workload.  `secondary` holds the 2 GiB KV-cache workload (NVFP4 ScaleSweep
+MSE [-3, 7] with a fused 16-point Hadamard; quantize and dequantize timed
+separately) and a plain device copy as the achievable-bandwidth reference.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBPS = 8000.0
+METRIC = "quantized Gelem/s + achieved HBM GB/s (% of peak), NVFP4 ScaleSweep MSE"
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=10)
+    p.add_argument("--copies", type=int, default=4, help="input copies cycled per step")
+    p.add_argument("--no-secondary", action="store_true")
+    p.add_argument("--no-cpu", action="store_true")
+    p.add_argument("--cpu-rows", type=int, default=2048)
+    return p.parse_args()
+
+
+def to_dev(x, dev):
+    import torch
+    if x.dtype == np.uint16:
+        return torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).to(dev)
+    return torch.from_numpy(x).to(dev)
+
+
+def event_time(fn, steps, warmup):
+    """Average ms per call of fn(i) over `steps` calls, HIP events on the
+    current stream (the stream every library call is issued on)."""
+    import torch
+    for i in range(warmup):
+        fn(i)
+    torch.cuda.synchronize()
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    s.record()
+    for i in range(steps):
+        fn(i)
+    e.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    return s.elapsed_time(e) / steps, wall
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one MI355X only: this build has no multi-GPU path "
+              "(the quantizer shards by rows with one all-reduce(max) of the global "
+              "scale; see DESIGN.md).  Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from block_scaled_fp4_fp4q_amd import binding as B
+    from block_scaled_fp4_fp4q_amd import synth
+
+    dev = torch.device("cuda:0")
+    B.lib()
+    log("device", torch.cuda.get_device_name(0))
+
+    # ---------------- headline: NVFP4 ScaleSweep WMSE on bf16 14336x4096 ----------------
+    rows, cols = synth.SHAPES["c2"]
+    t = time.time()
+    x_h, imp_h = synth.c2()
+    log(f"generated c2 {rows}x{cols} in {time.time() - t:.1f}s")
+    n = rows * cols
+    xs = [to_dev(x_h, dev)]
+    for _ in range(args.copies - 1):
+        xs.append(xs[0].clone())
+    imp = to_dev(imp_h, dev)
+    spec = B.make_spec(B.FP4Q_NVFP4, B.FP4Q_SCALE_SWEEP, B.FP4Q_OBJ_WMSE, (-8, 7))
+    spec_given = B.make_spec(B.FP4Q_NVFP4, B.FP4Q_SCALE_SWEEP, B.FP4Q_OBJ_WMSE, (-8, 7),
+                             global_scale_given=True)
+    ws = B.alloc_workspace(spec, rows, cols, dev)
+    outs = [(torch.empty(n // 2, dtype=torch.uint8, device=dev),
+             torch.empty(n // 16, dtype=torch.uint8, device=dev),
+             torch.empty(1, dtype=torch.float32, device=dev)) for _ in range(args.copies)]
+
+    def step(i):
+        c, s, g = outs[i % args.copies]
+        B.fp4q_quantize(spec, xs[i % args.copies], imp, c, s, g, ws)
+
+    ms, wall = event_time(step, args.steps, args.warmup)
+    log(f"full call: {ms * 1e3:.1f} us/step (wall {wall:.3f}s for {args.steps})")
+
+    def sweep_only(i):
+        c, s, g = outs[i % args.copies]
+        B.fp4q_quantize(spec_given, xs[i % args.copies], imp, c, s, g, ws)
+
+    ms_k, _ = event_time(sweep_only, args.steps, args.warmup)
+    bytes_per_elem_kernel = 2.0 + 0.5 + 1.0 / 16       # read bf16, write codes + scales
+    bytes_per_elem_call = 2 * 2.0 + 0.5 + 1.0 / 16     # + the global-max read
+    kernel_gbps = n * bytes_per_elem_kernel / (ms_k * 1e-3) / 1e9
+    call_gbps = n * bytes_per_elem_call / (ms * 1e-3) / 1e9
+    log(f"sweep kernel alone: {ms_k * 1e3:.1f} us, {kernel_gbps:.0f} GB/s")
+
+    # quality: ScaleSweep vs AbsMax MSE on the same tensor
+    c, s, g = outs[0]
+    B.fp4q_quantize(spec, xs[0], imp, c, s, g, ws)
+    mse_sweep, wmse_sweep = B.fp4q_error(B.make_spec(), xs[0], imp, c, s, g, ws)
+    ca, sa, ga = B.quantize(xs[0])
+    mse_abs, wmse_abs = B.error(xs[0], ca, sa, ga, importance=imp)
+    torch.cuda.synchronize()
+
+    result = {
+        "metric": METRIC,
+        "value": n / (ms * 1e-3) / 1e9,
+        "unit": "Gelem/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": "NVFP4 ScaleSweep WMSE [-8,7], bf16 weight 14336x4096 (t(4)*0.02), "
+                        "lognormal(0,1) column importance, global scale computed on device",
+            "rows": rows, "cols": cols, "block": 16, "input_dtype": "bf16",
+            "input_copies_cycled": args.copies,
+        },
+        "achieved_gbps": call_gbps,
+        "frac_of_peak": call_gbps / PEAK_HBM_GBPS,
+        "algorithmic_bytes_per_elem": bytes_per_elem_call,
+        "nvfp4_sweep_mse": mse_sweep,
+        "nvfp4_sweep_wmse": wmse_sweep,
+        "nvfp4_absmax_mse": mse_abs,
+        "nvfp4_absmax_wmse": wmse_abs,
+        "roofline": {
+            "kernel": "nvfp4_quant<bf16, no rotation, sweep, wmse>",
+            "bound": "hbm",
+            "achieved": kernel_gbps,
+            "peak": PEAK_HBM_GBPS,
+            "unit": "GB/s",
+            "frac": kernel_gbps / PEAK_HBM_GBPS,
+            "traffic": None,
+            "kernel_ms": ms_k,
+            "algorithmic_bytes_per_launch": n * bytes_per_elem_kernel,
+        },
+    }
+
+    # ---------------- CPU oracle on a row sample of the same workload ----------------
+    if not args.no_cpu:
+        from oracle import ref
+        cores = len(os.sched_getaffinity(0))
+        r = min(args.cpu_rows, rows)
+        xs_h = np.ascontiguousarray(x_h[:r])
+        t = time.perf_counter()
+        ref.quantize(xs_h, rule=ref.SWEEP, objective=ref.WMSE, importance=imp_h, nthreads=cores)
+        dt = time.perf_counter() - t
+        result["cpu_baseline"] = {
+            "value": r * cols / dt / 1e9, "unit": "Gelem/s", "cores": cores, "kind": "oracle",
+            "sample": f"first {r} of {rows} rows ({r * cols} elements), same quantize "
+                      f"(global max + ScaleSweep WMSE), {dt:.2f}s wall",
+        }
+        log(f"cpu oracle: {r * cols / dt / 1e6:.2f} Melem/s on {cores} threads")
+
+    # ---------------- secondary: KV cache, sweep MSE + fused Hadamard ----------------
+    if not args.no_secondary:
+        del xs, outs
+        torch.cuda.empty_cache()
+        t = time.time()
+        kv_h = synth.c5()
+        log(f"generated c5 {kv_h.shape} in {time.time() - t:.1f}s")
+        kv = to_dev(kv_h, dev)
+        del kv_h
+        kr, kc = kv.shape
+        kn = kr * kc
+        kspec = B.make_spec(B.FP4Q_NVFP4, B.FP4Q_SCALE_SWEEP, B.FP4Q_OBJ_MSE, (-3, 7), rotate=16)
+        kspec_g = B.make_spec(B.FP4Q_NVFP4, B.FP4Q_SCALE_SWEEP, B.FP4Q_OBJ_MSE, (-3, 7), rotate=16,
+                              global_scale_given=True)
+        kc_, ks_, kg_ = (torch.empty(kn // 2, dtype=torch.uint8, device=dev),
+                         torch.empty(kn // 16, dtype=torch.uint8, device=dev),
+                         torch.empty(1, dtype=torch.float32, device=dev))
+        ksteps = max(5, args.steps // 5)
+        kms, _ = event_time(lambda i: B.fp4q_quantize(kspec, kv, None, kc_, ks_, kg_, ws), ksteps, 2)
+        kms_k, _ = event_time(lambda i: B.fp4q_quantize(kspec_g, kv, None, kc_, ks_, kg_, ws), ksteps, 2)
+        y = torch.empty_like(kv)
+        dms, _ = event_time(lambda i: B.fp4q_dequantize(kspec, kc_, ks_, kg_, kr, kc, 16, y), ksteps, 2)
+        kmse, _ = B.fp4q_error(kspec, kv, None, kc_, ks_, kg_, ws)
+        ka, kas, kag = B.quantize(kv, rotate=16)
+        kmse_abs, _ = B.error(kv, ka, kas, kag, rotate=16)
+        del ka, kas
+        big = torch.empty(kn, dtype=torch.bfloat16, device=dev)
+        cms, _ = event_time(lambda i: big.copy_(kv.view(-1)), ksteps, 2)
+        torch.cuda.synchronize()
+        result["secondary"] = {
+            "kv_cache_sweep_mse_hadamard16": {
+                "workload": "NVFP4 ScaleSweep MSE [-3,7] + fused 16-point Hadamard, bf16 KV cache "
+                            "[64,32,4096,128] (2 GiB), global scale computed on device",
+                "quantize_ms": kms,
+                "quantize_gelem_s": kn / (kms * 1e-3) / 1e9,
+                "quantize_gbps": kn * 4.5625 / (kms * 1e-3) / 1e9,
+                "quantize_frac_of_peak": kn * 4.5625 / (kms * 1e-3) / 1e9 / PEAK_HBM_GBPS,
+                "sweep_kernel_ms": kms_k,
+                "sweep_kernel_gbps": kn * 2.5625 / (kms_k * 1e-3) / 1e9,
+                "dequantize_ms": dms,
+                "dequantize_gbps": kn * 2.5625 / (dms * 1e-3) / 1e9,
+                "nvfp4_sweep_mse": kmse,
+                "nvfp4_absmax_mse": kmse_abs,
+            },
+            "device_copy_gbps": 2 * kn * 2 / (cms * 1e-3) / 1e9,
+        }
+        log(f"c5 quantize {kms:.3f} ms, sweep kernel {kms_k:.3f} ms, dequant {dms:.3f} ms, "
+            f"copy {2 * kn * 2 / (cms * 1e-3) / 1e9:.0f} GB/s")
+
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

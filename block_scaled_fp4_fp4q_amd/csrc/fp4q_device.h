@@ -82,6 +82,58 @@ __device__ __forceinline__ float e2m1_value(uint32_t m)
     return e == 0 ? 0.5f * (float)f : __uint_as_float(((e + 126u) << 23) | (f << 22));
 }
 
+// ---- gfx950 FP4 conversion instructions ------------------------------------
+// v_cvt_scalef32_pk_fp4_f32 with a unit scale rounds two binary32 values to
+// the nearest E2M1 value (ties to the even code), saturates at +-6 and keeps
+// the sign (also of zero): exactly e2m1_q, applied to signed values.  It
+// writes the two codes as nibbles (first value low) into byte SEL of `old`.
+// v_cvt_scalef32_pk_f32_fp4 decodes byte SEL of a packed word.
+template <int SEL>
+__device__ __forceinline__ uint32_t fp4_pack2(uint32_t old, float a, float b)
+{
+    return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(old, a, b, 1.0f, SEL);
+}
+
+template <int SEL>
+__device__ __forceinline__ void fp4_unpack2(uint32_t packed, float& a, float& b)
+{
+    const auto t = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(packed, 1.0f, SEL);
+    a = t[0];
+    b = t[1];
+}
+
+// the same with a power-of-two scale P: codes of a/P and b/P, and P times the
+// decoded values (the hardware applies only the exponent of P, exactly)
+template <int SEL>
+__device__ __forceinline__ uint32_t fp4_pack2_scaled(uint32_t old, float a, float b, float P)
+{
+    return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(old, a, b, P, SEL);
+}
+
+template <int SEL>
+__device__ __forceinline__ void fp4_unpack2_scaled(uint32_t packed, float& a, float& b, float P)
+{
+    const auto t = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(packed, P, SEL);
+    a = t[0];
+    b = t[1];
+}
+
+// the 16 sign|magnitude nibbles of E2M1(v[i] * r), element 2k in the low
+// nibble of byte k
+__device__ __forceinline__ uint2 fp4_encode16(const float* v, float r)
+{
+    uint32_t lo = 0, hi = 0;
+    lo = fp4_pack2<0>(lo, v[0] * r, v[1] * r);
+    lo = fp4_pack2<1>(lo, v[2] * r, v[3] * r);
+    lo = fp4_pack2<2>(lo, v[4] * r, v[5] * r);
+    lo = fp4_pack2<3>(lo, v[6] * r, v[7] * r);
+    hi = fp4_pack2<0>(hi, v[8] * r, v[9] * r);
+    hi = fp4_pack2<1>(hi, v[10] * r, v[11] * r);
+    hi = fp4_pack2<2>(hi, v[12] * r, v[13] * r);
+    hi = fp4_pack2<3>(hi, v[14] * r, v[15] * r);
+    return make_uint2(lo, hi);
+}
+
 // INT4 step factor of IF4's 6/7 method: fl32(6/7)
 constexpr float kInt4Step = 0.857142865657806396484375f; // 0x3F5B6DB7
 

@@ -114,37 +114,6 @@ __global__ __launch_bounds__(1024) void finalize_scale(const float* __restrict__
 // encoders
 // ---------------------------------------------------------------------------
 
-// the 16 nibbles of an NVFP4 block encoded with step D (reciprocal r)
-__device__ __forceinline__ uint2 encode16_fp4(const float* v, float r)
-{
-    uint32_t lo = 0, hi = 0;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-        const uint32_t sgn = __float_as_uint(v[i]) >> 31;
-        const float q = e2m1_q(__builtin_fabsf(v[i]) * r);
-        const uint32_t nib = (sgn << 3) | e2m1_code(q);
-        if (i < 8)
-            lo |= nib << (4 * i);
-        else
-            hi |= nib << (4 * (i - 8));
-    }
-    return make_uint2(lo, hi);
-}
-
-__device__ __forceinline__ uint2 sign_only16(const float* v)
-{
-    uint32_t lo = 0, hi = 0;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-        const uint32_t nib = (__float_as_uint(v[i]) >> 31) << 3;
-        if (i < 8)
-            lo |= nib << (4 * i);
-        else
-            hi |= nib << (4 * (i - 8));
-    }
-    return make_uint2(lo, hi);
-}
-
 // block error of the FP4 encoding with step D, reciprocal r, in binary64
 template <bool WMSE>
 __device__ __forceinline__ double fp4_error16(const float* v, const float* w, float D, float r)
@@ -210,26 +179,15 @@ __device__ __forceinline__ void load_weights16(const float* __restrict__ imp, in
 }
 
 // ---------------------------------------------------------------------------
-// NVFP4: AbsMax or ScaleSweep (MSE / WMSE)
+// NVFP4 AbsMax
 // ---------------------------------------------------------------------------
 
-template <bool BF16, bool ROT, bool SWEEP, bool WMSE>
-__global__ __launch_bounds__(kThreads) void nvfp4_quant(
-    const void* __restrict__ x, int64_t nblocks, int64_t blocks_per_row,
-    const float* __restrict__ imp, const float* __restrict__ Sp, int lo, int hi,
+template <bool BF16, bool ROT>
+__global__ __launch_bounds__(kThreads) void nvfp4_absmax(
+    const void* __restrict__ x, int64_t nblocks, const float* __restrict__ Sp,
     uint2* __restrict__ codes, uint8_t* __restrict__ scales)
 {
-    __shared__ float sD[128], sR[128];
     const float S = *Sp;
-    if constexpr (SWEEP) {
-        // per-candidate step D = fl32(s*S) and reciprocal fl32(1/D), shared
-        for (int c = threadIdx.x; c < 128; c += kThreads) {
-            const float D = e4m3_value((uint32_t)(c < 0x7F ? c : 0x7E)) * S;
-            sD[c] = D;
-            sR[c] = 1.0f / D;
-        }
-        __syncthreads();
-    }
     const float S6 = 6.0f * S;
     for (int64_t blk = (int64_t)blockIdx.x * kThreads + threadIdx.x; blk < nblocks;
          blk += (int64_t)gridDim.x * kThreads) {
@@ -238,37 +196,265 @@ __global__ __launch_bounds__(kThreads) void nvfp4_quant(
         if constexpr (ROT)
             fwht<16>(v);
         const float a = block_absmax<16>(v);
-        uint2 packed;
-        uint32_t sbyte;
-        if (a == 0.0f) {
-            sbyte = 0;
-            packed = sign_only16(v);
-        } else {
-            uint32_t sb = e4m3_round(a / S6);
+        uint32_t sb = 0;
+        float r = 1.0f; // an all-zero block keeps only its signs
+        if (a != 0.0f) {
+            sb = e4m3_round(a / S6);
             sb = sb < 1u ? 1u : sb;
-            uint32_t cb = sb;
-            if constexpr (SWEEP) {
+            r = 1.0f / (e4m3_value(sb) * S);
+        }
+        codes[blk] = fp4_encode16(v, r);
+        scales[blk] = (uint8_t)sb;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// NVFP4 ScaleSweep (MSE / WMSE)
+//
+// Fast path, per block: every candidate's error is estimated in binary32 in
+// units of its step D (y = |x| r with the method's own r = fl32(1/D), codes
+// from the hardware E2M1 conversion, which rounds exactly like the method, so
+// each code is the method's code; only the error arithmetic is shortened).
+// A rigorous bound T on |binary64 error - estimate| then certifies the pick:
+// when the runner-up minus its bound exceeds the best plus its bound, the
+// binary64 argmin (ties to the smaller byte) is the estimated one.  Blocks
+// that are not certified -- exact ties, near ties, all-on-grid blocks -- go to
+// a queue in LDS that the whole workgroup drains with the exact binary64
+// evaluation, so the result equals the binary64 sweep for every block.
+// ---------------------------------------------------------------------------
+
+// binary32 estimates of sum_i w_i (y_i - E2M1(y_i))^2 for y_i = v_i * r and,
+// when PAIR, also for y_i / 2 (the pattern eight steps up, whose step is
+// exactly 2D) in units of the first step: the hardware conversion applies the
+// power-of-two scale 2 exactly, so one multiply serves both candidates.
+template <bool WMSE, bool PAIR>
+__device__ __forceinline__ void fp4_err32(const float* v, const float* w, float r, float& F1, float& F2)
+{
+    F1 = 0.0f;
+    F2 = 0.0f;
+#pragma unroll
+    for (int g = 0; g < 2; ++g) {
+        float y[8], q[8], h[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+            y[j] = v[8 * g + j] * r;
+        uint32_t c = 0, c2 = 0;
+        c = fp4_pack2<0>(c, y[0], y[1]);
+        c = fp4_pack2<1>(c, y[2], y[3]);
+        c = fp4_pack2<2>(c, y[4], y[5]);
+        c = fp4_pack2<3>(c, y[6], y[7]);
+        fp4_unpack2<0>(c, q[0], q[1]);
+        fp4_unpack2<1>(c, q[2], q[3]);
+        fp4_unpack2<2>(c, q[4], q[5]);
+        fp4_unpack2<3>(c, q[6], q[7]);
+        if constexpr (PAIR) {
+            c2 = fp4_pack2_scaled<0>(c2, y[0], y[1], 2.0f);
+            c2 = fp4_pack2_scaled<1>(c2, y[2], y[3], 2.0f);
+            c2 = fp4_pack2_scaled<2>(c2, y[4], y[5], 2.0f);
+            c2 = fp4_pack2_scaled<3>(c2, y[6], y[7], 2.0f);
+            fp4_unpack2_scaled<0>(c2, h[0], h[1], 2.0f);
+            fp4_unpack2_scaled<1>(c2, h[2], h[3], 2.0f);
+            fp4_unpack2_scaled<2>(c2, h[4], h[5], 2.0f);
+            fp4_unpack2_scaled<3>(c2, h[6], h[7], 2.0f);
+        }
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const float d = y[j] - q[j];
+            F1 = __builtin_fmaf(WMSE ? d * w[8 * g + j] : d, d, F1);
+            if constexpr (PAIR) {
+                const float e = y[j] - h[j];
+                F2 = __builtin_fmaf(WMSE ? e * w[8 * g + j] : e, e, F2);
+            }
+        }
+    }
+}
+
+// clamp a window pattern into [0x01, 0x7E]: a pattern past an end stands for
+// the end pattern itself
+__device__ __forceinline__ int clamp_pattern(int c) { return c < 1 ? 1 : (c > 0x7E ? 0x7E : c); }
+
+// exact binary64 sweep of one block (the fallback); stores its codes and scale
+template <bool BF16, bool ROT, bool WMSE>
+__device__ __noinline__ void sweep_block_exact(const void* __restrict__ x, int64_t blk,
+                                               int64_t blocks_per_row, const float* __restrict__ imp,
+                                               const float4* tab, float S6, int lo, int hi,
+                                               uint2* __restrict__ codes, uint8_t* __restrict__ scales)
+{
+    float v[16];
+    load_block<16, BF16, false>(x, blk, v);
+    if constexpr (ROT)
+        fwht<16>(v);
+    const float a = block_absmax<16>(v);
+    uint32_t sb = e4m3_round(a / S6);
+    sb = sb < 1u ? 1u : sb;
+    float w[16];
+    if constexpr (WMSE)
+        load_weights16(imp, (blk % blocks_per_row) * 16, w);
+    double best = __builtin_huge_val();
+    int cb = -1, cprev = -1;
+    for (int k = lo; k <= hi; ++k) {
+        const int c = clamp_pattern((int)sb + k);
+        if (c == cprev)
+            continue;
+        cprev = c;
+        const float4 t = tab[c];
+        const double E = fp4_error16<WMSE>(v, w, t.x, t.y);
+        if (E < best) {
+            best = E;
+            cb = c;
+        }
+    }
+    codes[blk] = fp4_encode16(v, tab[cb].y);
+    scales[blk] = (uint8_t)cb;
+}
+
+// keep the least and the second least estimate; ties keep the earlier one
+__device__ __forceinline__ void keep_best(float E, int c, float& e1, float& e2, int& cb)
+{
+    const bool better = E < e1;
+    e2 = better ? e1 : __builtin_fminf(e2, E);
+    cb = better ? c : cb;
+    e1 = better ? E : e1;
+}
+
+constexpr int kQueueCap = 1024; // fallback queue entries per workgroup (LDS)
+
+template <bool BF16, bool ROT, bool WMSE>
+__global__ __launch_bounds__(kThreads) void nvfp4_sweep(
+    const void* __restrict__ x, int64_t nblocks, int64_t blocks_per_row,
+    const float* __restrict__ imp, const float* __restrict__ Sp, int lo, int hi,
+    uint2* __restrict__ codes, uint8_t* __restrict__ scales)
+{
+    // per pattern: D = fl32(s S), r = fl32(1/D), fl32(D*D), and 1 when the
+    // pattern eight steps up has exactly twice this step (so one product
+    // serves both), else 0
+    __shared__ float4 tab[128];
+    __shared__ int64_t queue[kQueueCap];
+    __shared__ uint32_t qn;
+    const float S = *Sp;
+    for (int c = threadIdx.x; c < 128; c += kThreads) {
+        const float D = e4m3_value((uint32_t)(c < 0x7E ? c : 0x7E)) * S;
+        const float D8 = e4m3_value((uint32_t)(c + 8 < 0x7E ? c + 8 : 0x7E)) * S;
+        const bool twice = c >= 8 && c + 8 <= 0x7E && D8 == 2.0f * D && (1.0f / D8) == 0.5f * (1.0f / D);
+        tab[c] = make_float4(D, 1.0f / D, D * D, twice ? 1.0f : 0.0f);
+    }
+    if (threadIdx.x == 0)
+        qn = 0;
+    __syncthreads();
+    const float S6 = 6.0f * S;
+    constexpr float u = 0x1p-24f; // unit roundoff of binary32
+    const int64_t stride = (int64_t)gridDim.x * kThreads;
+    // importance column of this lane's block, advanced incrementally
+    int64_t col = 0, col_step = 0;
+    if constexpr (WMSE) {
+        col = ((int64_t)blockIdx.x * kThreads + threadIdx.x) % blocks_per_row;
+        col_step = stride % blocks_per_row;
+    }
+
+    auto drain = [&]() {
+        const uint32_t n = qn;
+        for (uint32_t j = threadIdx.x; j < n; j += kThreads)
+            sweep_block_exact<BF16, ROT, WMSE>(x, queue[j], blocks_per_row, imp, tab, S6, lo, hi,
+                                               codes, scales);
+        __syncthreads();
+        if (threadIdx.x == 0)
+            qn = 0;
+        __syncthreads();
+    };
+
+    // every thread runs the same number of iterations, so the barriers below
+    // are reached uniformly
+    for (int64_t base = (int64_t)blockIdx.x * kThreads; base < nblocks; base += stride) {
+        const int64_t blk = base + threadIdx.x;
+        if (blk < nblocks) {
+            float v[16];
+            load_block<16, BF16>(x, blk, v);
+            if constexpr (ROT)
+                fwht<16>(v);
+            const float a = block_absmax<16>(v);
+            bool queued = false;
+            if (a == 0.0f) {
+                codes[blk] = fp4_encode16(v, 1.0f); // signs only
+                scales[blk] = 0;
+            } else {
+                uint32_t sb = e4m3_round(a / S6);
+                sb = sb < 1u ? 1u : sb;
+                // this lane's offsets that land on finite patterns
+                const int klo = max(lo, 1 - (int)sb), khi = min(hi, 0x7E - (int)sb);
                 float w[16];
-                if constexpr (WMSE)
-                    load_weights16(imp, (blk % blocks_per_row) * 16, w);
-                const int c0 = max(1, (int)sb + lo), c1 = min(0x7E, (int)sb + hi);
-                double best = __builtin_huge_val();
-                for (int c = c0; c <= c1; ++c) {
-                    const double E = fp4_error16<WMSE>(v, w, sD[c], sR[c]);
-                    if (E < best) {
-                        best = E;
-                        cb = (uint32_t)c;
+                float W = 16.0f;
+                if constexpr (WMSE) {
+                    load_weights16(imp, col * 16, w);
+                    W = 0.0f;
+#pragma unroll
+                    for (int i = 0; i < 16; ++i)
+                        W += w[i];
+                }
+                float e1 = __builtin_huge_valf(), e2 = __builtin_huge_valf();
+                int cb = 1;
+                // offsets k and k+8 pair up in runs of eight; the rest are singles
+                for (int k = lo; k <= hi; ++k) {
+                    if (((k - lo) & 15) >= 8)
+                        continue; // evaluated with its partner k-8 (uniform branch)
+                    const bool ok1 = k >= klo && k <= khi;
+                    const int c = clamp_pattern((int)sb + k);
+                    const float4 t = tab[c];
+                    if (k + 8 <= hi) {
+                        const bool ok2 = k + 8 >= klo && k + 8 <= khi;
+                        const int c8 = clamp_pattern((int)sb + k + 8);
+                        float F1, F2, E2;
+                        if (__builtin_amdgcn_ballot_w64(t.w == 0.0f) == 0) {
+                            // every lane's pair is an exact doubling: shared product
+                            fp4_err32<WMSE, true>(v, w, t.y, F1, F2);
+                            E2 = F2 * t.z;
+                        } else {
+                            float unused;
+                            fp4_err32<WMSE, false>(v, w, t.y, F1, unused);
+                            fp4_err32<WMSE, false>(v, w, tab[c8].y, F2, unused);
+                            E2 = F2 * tab[c8].z;
+                        }
+                        keep_best(ok1 ? F1 * t.z : __builtin_huge_valf(), c, e1, e2, cb);
+                        keep_best(ok2 ? E2 : __builtin_huge_valf(), c8, e1, e2, cb);
+                    } else {
+                        float F1, unused;
+                        fp4_err32<WMSE, false>(v, w, t.y, F1, unused);
+                        keep_best(ok1 ? F1 * t.z : __builtin_huge_valf(), c, e1, e2, cb);
                     }
                 }
+                // |binary64 error - estimate| <= T(estimate): 5u|y| per element
+                // from the shortened arithmetic, summed by Cauchy-Schwarz, plus
+                // the binary32 accumulation; constants carry >= 50% slack
+                const float A = __builtin_fmaxf(a, 6.0f * tab[clamp_pattern((int)sb + hi)].x) * (1.0f + 4.0f * u);
+                const float tail = 64.0f * u * u * A * A * W;
+                const float s1 = __builtin_amdgcn_sqrtf(W * e1) * 1.0001f;
+                const float s2 = __builtin_amdgcn_sqrtf(W * e2) * 1.0001f;
+                const float t1 = 16.0f * u * A * s1 + 32.0f * u * e1 + tail;
+                const float t2 = 16.0f * u * A * s2 + 32.0f * u * e2 + tail;
+                const bool certain = klo <= khi && e1 < __builtin_huge_valf() &&
+                                     ((e2 == __builtin_huge_valf()) || (e2 - t2 > e1 + t1));
+                if (certain) {
+                    codes[blk] = fp4_encode16(v, tab[cb].y);
+                    scales[blk] = (uint8_t)cb;
+                } else {
+                    queued = true;
+                }
             }
-            const float D = e4m3_value(cb) * S;
-            const float r = 1.0f / D;
-            sbyte = cb;
-            packed = encode16_fp4(v, r);
+            if (queued) {
+                const uint32_t slot = atomicAdd(&qn, 1u); // < kQueueCap, see below
+                queue[slot] = blk;
+            }
         }
-        codes[blk] = packed;
-        scales[blk] = (uint8_t)sbyte;
+        if constexpr (WMSE) {
+            col += col_step;
+            col = col >= blocks_per_row ? col - blocks_per_row : col;
+        }
+        __syncthreads();
+        // at most kThreads entries join per iteration: drain before overflow
+        if (qn > (uint32_t)(kQueueCap - kThreads))
+            drain();
     }
+    __syncthreads();
+    drain();
 }
 
 // ---------------------------------------------------------------------------
@@ -294,7 +480,7 @@ __global__ __launch_bounds__(kThreads) void if4_quant(
         uint32_t sbyte;
         if (a == 0.0f) {
             sbyte = 0;
-            packed = sign_only16(v);
+            packed = fp4_encode16(v, 1.0f); // signs only
         } else {
             uint32_t sb = e4m3_round(a / S6);
             sb = sb < 1u ? 1u : sb;
@@ -312,7 +498,7 @@ __global__ __launch_bounds__(kThreads) void if4_quant(
                 packed = encode16_int4(v, ri);
             } else {
                 sbyte = sb;
-                packed = encode16_fp4(v, r);
+                packed = fp4_encode16(v, r);
             }
         }
         codes[blk] = packed;
@@ -524,20 +710,46 @@ static int grid_for(int64_t items, int cap)
 
 constexpr int kQuantGroupCap = 16384;
 
+// one full round of resident workgroups of `kernel` (every compute unit
+// filled once), so that grid-stride kernels amortize their prologue
+template <typename K>
+static int resident_groups(K kernel)
+{
+    int dev = 0, cus = 0, per_cu = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, kThreads, 0) != hipSuccess)
+        return 2048;
+    return per_cu > 0 && cus > 0 ? per_cu * cus : 2048;
+}
+
+template <typename K>
+static int sweep_grid(K kernel, int64_t nb)
+{
+    static thread_local int cache_dev = -1;
+    (void)cache_dev;
+    const int64_t need = (nb + kThreads - 1) / kThreads;
+    const int cap = resident_groups(kernel);
+    return (int)(need < cap ? (need < 1 ? 1 : need) : cap);
+}
+
 template <bool BF16, bool ROT>
 static void launch_nvfp4(const QuantArgs& a, int64_t nb, const float* Sp, int grid)
 {
     const int64_t bpr = a.cols / 16;
     uint2* codes = reinterpret_cast<uint2*>(a.codes);
-    if (a.rule == kAbsMax)
-        hipLaunchKernelGGL((nvfp4_quant<BF16, ROT, false, false>), grid, kThreads, 0, a.stream,
-                           a.x, nb, bpr, a.importance, Sp, 0, 0, codes, a.scales);
-    else if (a.objective == kWMSE)
-        hipLaunchKernelGGL((nvfp4_quant<BF16, ROT, true, true>), grid, kThreads, 0, a.stream,
+    if (a.rule == kAbsMax) {
+        hipLaunchKernelGGL((nvfp4_absmax<BF16, ROT>), grid, kThreads, 0, a.stream,
+                           a.x, nb, Sp, codes, a.scales);
+    } else if (a.objective == kWMSE) {
+        auto k = nvfp4_sweep<BF16, ROT, true>;
+        hipLaunchKernelGGL(k, sweep_grid(k, nb), kThreads, 0, a.stream,
                            a.x, nb, bpr, a.importance, Sp, a.lo, a.hi, codes, a.scales);
-    else
-        hipLaunchKernelGGL((nvfp4_quant<BF16, ROT, true, false>), grid, kThreads, 0, a.stream,
+    } else {
+        auto k = nvfp4_sweep<BF16, ROT, false>;
+        hipLaunchKernelGGL(k, sweep_grid(k, nb), kThreads, 0, a.stream,
                            a.x, nb, bpr, a.importance, Sp, a.lo, a.hi, codes, a.scales);
+    }
 }
 
 template <bool BF16, bool ROT>
