@@ -1,0 +1,170 @@
+"""Full-size parity on the five workloads, through the C ABI.
+
+c1, c3 and c4 are compared with the oracle on every block.  For c2 and c5 the
+GPU quantizes the whole tensor; the global scale is checked against the
+oracle's rule applied to the exact tensor maximum (computed on the host), and
+the oracle then re-quantizes a seeded sample of rows under that scale, which
+must match byte for byte.  Dequantized values are bit-exact where compared;
+the reported MSE/WMSE must agree with the oracle's full-tensor value to
+1e-9 relative (binary64 sums in different orders)."""
+import os
+
+import numpy as np
+import pytest
+import torch
+
+from block_scaled_fp4_fp4q_amd import synth
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+THREADS = min(16, len(os.sched_getaffinity(0)))
+
+
+@pytest.fixture(scope="module")
+def B():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from block_scaled_fp4_fp4q_amd import binding
+    binding.lib()
+    return binding
+
+
+def to_dev(x):
+    if x.dtype == np.uint16:
+        return torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).to(DEV)
+    return torch.from_numpy(x).to(DEV)
+
+
+def near_ties(best, second):
+    live = best > 0
+    gap = np.where(live, (second - best) / np.where(live, best, 1.0), np.inf)
+    return int(np.sum(gap < 1e-6))
+
+
+def compare_rows(ref, x, rows, got_codes, got_scales, S, B_, **kw):
+    """Oracle re-quantization of `rows` under global scale S vs the GPU."""
+    cols = x.shape[1]
+    xs = np.ascontiguousarray(x[rows])
+    want = ref.quantize(xs, global_scale=S, nthreads=THREADS, errors=True, **kw)
+    nb_row = cols // B_
+    gs = got_scales.reshape(-1, nb_row)[rows].reshape(-1)
+    gc = got_codes.reshape(-1, cols // 2)[rows].reshape(-1)
+    bad = np.nonzero(gs != want["scales"])[0]
+    assert bad.size == 0, f"{bad.size} scale mismatches, first {bad[:5]}"
+    assert np.array_equal(gc, want["codes"])
+    return want
+
+
+def test_c1_full(B, ref):
+    x = synth.c1()
+    xd = to_dev(x)
+    for rule in (0, 1):
+        codes, scales, gs = B.quantize(xd, scale_rule=rule)
+        want = ref.quantize(x, rule=rule, nthreads=THREADS, errors=True)
+        assert gs.item() == np.float32(want["S"])
+        assert np.array_equal(scales.cpu().numpy(), want["scales"])
+        assert np.array_equal(codes.cpu().numpy(), want["codes"])
+        mse = B.error(xd, codes, scales, gs)[0]
+        assert abs(mse - ref.error(x, want["codes"], want["scales"], want["S"])[0]) <= 1e-9 * mse
+        print(f"c1 rule={rule}: near-tie blocks {near_ties(want['best'], want['second'])}")
+
+
+@pytest.fixture(scope="module")
+def c2data():
+    return synth.c2()
+
+
+def test_c2_sweep_wmse(B, ref, c2data):
+    x, imp = c2data
+    xd, impd = to_dev(x), to_dev(imp)
+    codes, scales, gs = B.quantize(xd, scale_rule=1, objective=1, window=(-8, 7), importance=impd)
+    torch.cuda.synchronize()
+    S = gs.item()
+    G = np.abs(synth.bf16_bits_to_f32(x)).max()
+    assert S == ref.lib().fp4q_ref_global_scale(G)
+    rows = synth.rows_sample(x, 1024, seed=2)
+    want = compare_rows(ref, x, rows, codes.cpu().numpy(), scales.cpu().numpy(), S, 16,
+                        rule=ref.SWEEP, objective=ref.WMSE, importance=imp)
+    print(f"c2: sampled {len(rows)} rows, near-tie blocks {near_ties(want['best'], want['second'])}")
+    mse, wmse = B.error(xd, codes, scales, gs, importance=impd)
+    # oracle on the full tensor: its own quantization must give the same MSE
+    full = ref.quantize(x, rule=ref.SWEEP, objective=ref.WMSE, importance=imp, nthreads=THREADS)
+    assert np.array_equal(full["scales"], scales.cpu().numpy())
+    assert np.array_equal(full["codes"], codes.cpu().numpy())
+    e = ref.error(x, full["codes"], full["scales"], full["S"], importance=imp, nthreads=THREADS)
+    assert abs(mse - e[0]) <= 1e-9 * e[0] and abs(wmse - e[1]) <= 1e-9 * e[1]
+
+
+def test_c2_absmax_and_dequant(B, ref, c2data):
+    x, imp = c2data
+    xd = to_dev(x)
+    codes, scales, gs = B.quantize(xd)
+    full = ref.quantize(x, nthreads=THREADS)
+    assert np.array_equal(full["scales"], scales.cpu().numpy())
+    assert np.array_equal(full["codes"], codes.cpu().numpy())
+    y = B.dequantize(codes, scales, gs, *x.shape, dtype=torch.bfloat16)
+    rows = synth.rows_sample(x, 512, seed=5)
+    yw = ref.dequantize(full["codes"], full["scales"], full["S"], *x.shape, out_dtype=ref.BF16,
+                        nthreads=THREADS)
+    yg = y.view(torch.int16).cpu().numpy().view(np.uint16)
+    assert np.array_equal(yg[rows], yw[rows])
+
+
+@pytest.mark.parametrize("rotate", [0, 32])
+def test_c3_mxfp4(B, ref, rotate):
+    x = synth.c3()
+    xd = to_dev(x)
+    codes, scales, _ = B.quantize(xd, format=B.FP4Q_MXFP4, rotate=rotate)
+    want = ref.quantize(x, fmt=ref.MXFP4, rotate=rotate, nthreads=THREADS)
+    assert np.array_equal(scales.cpu().numpy(), want["scales"])
+    assert np.array_equal(codes.cpu().numpy(), want["codes"])
+    mse = B.error(xd, codes, scales, None, format=B.FP4Q_MXFP4, rotate=rotate)[0]
+    e = ref.error(x, want["codes"], want["scales"], None, fmt=ref.MXFP4, rotate=rotate, nthreads=THREADS)[0]
+    assert abs(mse - e) <= 1e-9 * e
+    print(f"c3 rotate={rotate}: MSE {mse:.6g}")
+
+
+def test_c4_if4(B, ref):
+    x, uniform = synth.c4()
+    xd = to_dev(x)
+    codes, scales, gs = B.quantize(xd, format=B.FP4Q_IF4)
+    want = ref.quantize(x, fmt=ref.IF4, nthreads=THREADS)
+    assert gs.item() == np.float32(want["S"])
+    s = scales.cpu().numpy()
+    assert np.array_equal(s, want["scales"])
+    assert np.array_equal(codes.cpu().numpy(), want["codes"])
+    ind = (s & 0x80) != 0
+    print(f"c4: INT4 share uniform {ind[uniform].mean():.3f}, spiky {ind[~uniform].mean():.3f}")
+    y = B.dequantize(codes, scales, gs, *x.shape, format=B.FP4Q_IF4)
+    rows = synth.rows_sample(x, 256, seed=4)
+    sub = ref.dequantize(want["codes"].reshape(x.shape[0], -1)[rows].reshape(-1),
+                         want["scales"].reshape(x.shape[0], -1)[rows].reshape(-1),
+                         want["S"], len(rows), x.shape[1], fmt=ref.IF4)
+    assert np.array_equal(y.cpu().numpy()[rows].view(np.uint32), sub.view(np.uint32))
+
+
+def test_c5_kv_sweep_hadamard(B, ref):
+    x = synth.c5()
+    xd = to_dev(x)
+    codes, scales, gs = B.quantize(xd, scale_rule=1, objective=0, window=(-3, 7), rotate=16)
+    torch.cuda.synchronize()
+    S = gs.item()
+    xr = ref.prepare(x, rotate=16, nthreads=THREADS)     # rotated, widened (4 GiB)
+    G = float(np.abs(xr).max())
+    del xr
+    assert S == ref.lib().fp4q_ref_global_scale(np.float32(G))
+    rows = synth.rows_sample(x, 8192, seed=5)
+    gc, gsc = codes.cpu().numpy(), scales.cpu().numpy()
+    want = compare_rows(ref, x, rows, gc, gsc, S, 16, rule=ref.SWEEP, objective=ref.MSE, rotate=16)
+    print(f"c5: sampled {len(rows)} rows, near-tie blocks {near_ties(want['best'], want['second'])}")
+    # dequantize round trip (un-rotated, bf16) on the sampled rows
+    y = B.dequantize(codes, scales, gs, *x.shape, unrotate=16, dtype=torch.bfloat16)
+    yg = y.view(torch.int16).cpu().numpy().view(np.uint16)[rows]
+    del y
+    yw = ref.dequantize(want["codes"], want["scales"], S, len(rows), x.shape[1], unrotate=16,
+                        out_dtype=ref.BF16)
+    assert np.array_equal(yg, yw)
+    mse = B.error(xd, codes, scales, gs, rotate=16)[0]
+    e = ref.error(x, gc, gsc, S, rotate=16, nthreads=THREADS)[0]
+    assert abs(mse - e) <= 1e-9 * e
+    print(f"c5: MSE {mse:.6g}")
