@@ -12,9 +12,10 @@ Printed: one JSON line (rank 0).  `value` is quantized Gelem/s of the whole
 call; `roofline` is the dominant kernel (the sweep quantizer) timed alone
 with HIP events on the stream it runs on, against the 8 TB/s HBM peak;
 `cpu_baseline` is the CPU oracle on a bounded row sample of the same
-workload.  `secondary` holds the 2 GiB KV-cache workload (NVFP4 ScaleSweep
-MSE [-3, 7] with a fused 16-point Hadamard; quantize and dequantize timed
-separately) and a plain device copy as the achievable-bandwidth reference.
+workload, and `parity_sample` compares the GPU's bytes on those rows with the
+oracle's.  `secondary` holds the 2 GiB KV-cache workload (NVFP4 ScaleSweep MSE
+[-3, 7] with a fused 16-point Hadamard; quantize and dequantize timed
+separately).  A plain 1 GiB device copy is the achievable-bandwidth yardstick.
 """
 import argparse
 import json
@@ -29,6 +30,36 @@ sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBPS = 8000.0
 METRIC = "quantized Gelem/s + achieved HBM GB/s (% of peak), NVFP4 ScaleSweep MSE"
+
+
+COUNTERS = os.path.join(ROOT, "profiles", "nvfp4_sweep_wmse_hbm_counters.md")
+KERNEL_SOURCES = ["block_scaled_fp4_fp4q_amd/csrc/fp4q_kernels.hip",
+                  "block_scaled_fp4_fp4q_amd/csrc/fp4q_device.h"]
+
+
+def kernel_source_hash():
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic():
+    """HBM bytes per launch of the sweep kernel from the committed rocprofv3
+    FETCH_SIZE/WRITE_SIZE summary, or None when the kernel sources changed
+    since those counters were taken."""
+    import re
+    try:
+        text = open(COUNTERS).read()
+    except OSError:
+        return None
+    h = re.search(r"Kernel sources sha256\[:16\] = `([0-9a-f]+)`", text)
+    t = re.search(r"traffic_bytes_per_launch \S+ = (\d+)", text)
+    if not h or not t or h.group(1) != kernel_source_hash():
+        return None
+    return int(t.group(1))
 
 
 def log(*a):
@@ -124,6 +155,16 @@ def main():
     call_gbps = n * bytes_per_elem_call / (ms * 1e-3) / 1e9
     log(f"sweep kernel alone: {ms_k * 1e3:.1f} us, {kernel_gbps:.0f} GB/s")
 
+    # reference: a plain device copy of 1 GiB (read + write, larger than the
+    # Infinity Cache) -- the achievable-bandwidth yardstick, and the kernel
+    # whose FETCH_SIZE / WRITE_SIZE calibrate the HBM traffic counters
+    ref_src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    ref_dst = torch.empty_like(ref_src)
+    cms, _ = event_time(lambda i: ref_dst.copy_(ref_src), 10, 2)
+    copy_gbps = 2 * ref_src.numel() / (cms * 1e-3) / 1e9
+    del ref_src, ref_dst
+    log(f"device copy 1 GiB: {copy_gbps:.0f} GB/s")
+
     # quality: ScaleSweep vs AbsMax MSE on the same tensor
     c, s, g = outs[0]
     B.fp4q_quantize(spec, xs[0], imp, c, s, g, ws)
@@ -152,6 +193,7 @@ def main():
             "input_copies_cycled": args.copies,
         },
         "achieved_gbps": call_gbps,
+        "device_copy_gbps": copy_gbps,
         "frac_of_peak": call_gbps / PEAK_HBM_GBPS,
         "algorithmic_bytes_per_elem": bytes_per_elem_call,
         "nvfp4_sweep_mse": mse_sweep,
@@ -159,13 +201,14 @@ def main():
         "nvfp4_absmax_mse": mse_abs,
         "nvfp4_absmax_wmse": wmse_abs,
         "roofline": {
-            "kernel": "nvfp4_quant<bf16, no rotation, sweep, wmse>",
+            "kernel": "nvfp4_sweep<bf16, no rotation, wmse>",
             "bound": "hbm",
             "achieved": kernel_gbps,
             "peak": PEAK_HBM_GBPS,
             "unit": "GB/s",
             "frac": kernel_gbps / PEAK_HBM_GBPS,
-            "traffic": None,
+            "traffic": measured_traffic(),
+            "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
             "kernel_ms": ms_k,
             "algorithmic_bytes_per_launch": n * bytes_per_elem_kernel,
         },
@@ -186,6 +229,24 @@ def main():
                       f"(global max + ScaleSweep WMSE), {dt:.2f}s wall",
         }
         log(f"cpu oracle: {r * cols / dt / 1e6:.2f} Melem/s on {cores} threads")
+        # the same rows re-quantized by the oracle under the GPU's global scale
+        c, s_, g = outs[0]
+        B.fp4q_quantize(spec, xs[0], imp, c, s_, g, ws)
+        torch.cuda.synchronize()
+        S = float(g.item())
+        want = ref.quantize(xs_h, rule=ref.SWEEP, objective=ref.WMSE, importance=imp_h,
+                            global_scale=S, nthreads=cores, errors=True)
+        gs_rows = s_.cpu().numpy()[: r * cols // 16]
+        gc_rows = c.cpu().numpy()[: r * cols // 2]
+        live = want["best"] > 0
+        gap = np.where(live, (want["second"] - want["best"]) / np.where(live, want["best"], 1), np.inf)
+        result["parity_sample"] = {
+            "blocks": int(gs_rows.size),
+            "scale_mismatches": int(np.sum(gs_rows != want["scales"])),
+            "code_bytes_mismatched": int(np.sum(gc_rows != want["codes"])),
+            "oracle_near_tie_blocks": int(np.sum(gap < 1e-6)),
+        }
+        log(f"parity on the sample: {result['parity_sample']}")
 
     # ---------------- secondary: KV cache, sweep MSE + fused Hadamard ----------------
     if not args.no_secondary:
@@ -213,8 +274,6 @@ def main():
         ka, kas, kag = B.quantize(kv, rotate=16)
         kmse_abs, _ = B.error(kv, ka, kas, kag, rotate=16)
         del ka, kas
-        big = torch.empty(kn, dtype=torch.bfloat16, device=dev)
-        cms, _ = event_time(lambda i: big.copy_(kv.view(-1)), ksteps, 2)
         torch.cuda.synchronize()
         result["secondary"] = {
             "kv_cache_sweep_mse_hadamard16": {
@@ -231,10 +290,8 @@ def main():
                 "nvfp4_sweep_mse": kmse,
                 "nvfp4_absmax_mse": kmse_abs,
             },
-            "device_copy_gbps": 2 * kn * 2 / (cms * 1e-3) / 1e9,
         }
-        log(f"c5 quantize {kms:.3f} ms, sweep kernel {kms_k:.3f} ms, dequant {dms:.3f} ms, "
-            f"copy {2 * kn * 2 / (cms * 1e-3) / 1e9:.0f} GB/s")
+        log(f"c5 quantize {kms:.3f} ms, sweep kernel {kms_k:.3f} ms, dequant {dms:.3f} ms")
 
     print(json.dumps(result), flush=True)
 
