@@ -36,6 +36,15 @@ __device__ __forceinline__ uint32_t f32_to_bf16(float f)
     return u >> 16;
 }
 
+// two binary32 values rounded to bf16 (nearest even) and packed, first value
+// in the low half: one v_cvt_pk_bf16_f32 on gfx950
+__device__ __forceinline__ uint32_t bf16_pair(float a, float b)
+{
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    const bf16x2 v = {(__bf16)a, (__bf16)b};
+    return __builtin_bit_cast(uint32_t, v);
+}
+
 // ---- E4M3FN --------------------------------------------------------------
 
 // value of a non-negative E4M3 pattern 0x00..0x7E

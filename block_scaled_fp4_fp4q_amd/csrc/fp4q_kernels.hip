@@ -273,41 +273,6 @@ __device__ __forceinline__ void fp4_err32(const float* v, const float* w, float 
 // the end pattern itself
 __device__ __forceinline__ int clamp_pattern(int c) { return c < 1 ? 1 : (c > 0x7E ? 0x7E : c); }
 
-// exact binary64 sweep of one block (the fallback); stores its codes and scale
-template <bool BF16, bool ROT, bool WMSE>
-__device__ __noinline__ void sweep_block_exact(const void* __restrict__ x, int64_t blk,
-                                               int64_t blocks_per_row, const float* __restrict__ imp,
-                                               const float4* tab, float S6, int lo, int hi,
-                                               uint2* __restrict__ codes, uint8_t* __restrict__ scales)
-{
-    float v[16];
-    load_block<16, BF16, false>(x, blk, v);
-    if constexpr (ROT)
-        fwht<16>(v);
-    const float a = block_absmax<16>(v);
-    uint32_t sb = e4m3_round(a / S6);
-    sb = sb < 1u ? 1u : sb;
-    float w[16];
-    if constexpr (WMSE)
-        load_weights16(imp, (blk % blocks_per_row) * 16, w);
-    double best = __builtin_huge_val();
-    int cb = -1, cprev = -1;
-    for (int k = lo; k <= hi; ++k) {
-        const int c = clamp_pattern((int)sb + k);
-        if (c == cprev)
-            continue;
-        cprev = c;
-        const float4 t = tab[c];
-        const double E = fp4_error16<WMSE>(v, w, t.x, t.y);
-        if (E < best) {
-            best = E;
-            cb = c;
-        }
-    }
-    codes[blk] = fp4_encode16(v, tab[cb].y);
-    scales[blk] = (uint8_t)cb;
-}
-
 // keep the least and the second least estimate; ties keep the earlier one
 __device__ __forceinline__ void keep_best(float E, int c, float& e1, float& e2, int& cb)
 {
@@ -320,7 +285,7 @@ __device__ __forceinline__ void keep_best(float E, int c, float& e1, float& e2, 
 constexpr int kQueueCap = 1024; // fallback queue entries per workgroup (LDS)
 
 template <bool BF16, bool ROT, bool WMSE>
-__global__ __launch_bounds__(kThreads) void nvfp4_sweep(
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) void nvfp4_sweep(
     const void* __restrict__ x, int64_t nblocks, int64_t blocks_per_row,
     const float* __restrict__ imp, const float* __restrict__ Sp, int lo, int hi,
     uint2* __restrict__ codes, uint8_t* __restrict__ scales)
@@ -351,11 +316,52 @@ __global__ __launch_bounds__(kThreads) void nvfp4_sweep(
         col_step = stride % blocks_per_row;
     }
 
+    // Exact binary64 sweep of the queued blocks, candidate-parallel: sixteen
+    // lanes share a block, each evaluates every sixteenth offset of the
+    // window, and the group keeps the least (error, pattern) pair -- the same
+    // choice as a scan in ascending order that keeps the first least error.
     auto drain = [&]() {
         const uint32_t n = qn;
-        for (uint32_t j = threadIdx.x; j < n; j += kThreads)
-            sweep_block_exact<BF16, ROT, WMSE>(x, queue[j], blocks_per_row, imp, tab, S6, lo, hi,
-                                               codes, scales);
+        const int grp = threadIdx.x >> 4, sub = threadIdx.x & 15;
+        for (uint32_t j0 = 0; j0 < n; j0 += kThreads / 16) {
+            const uint32_t j = j0 + grp;
+            const bool active = j < n;
+            const int64_t blk = queue[active ? j : 0];
+            float v[16];
+            load_block<16, BF16, false>(x, blk, v);
+            if constexpr (ROT)
+                fwht<16>(v);
+            const float a = block_absmax<16>(v);
+            uint32_t sb = e4m3_round(a / S6);
+            sb = sb < 1u ? 1u : sb;
+            float w[16];
+            if constexpr (WMSE)
+                load_weights16(imp, (blk % blocks_per_row) * 16, w);
+            double best = __builtin_huge_val();
+            int cb = 0x7F;
+            for (int k = lo + sub; k <= hi; k += 16) {
+                const int c = clamp_pattern((int)sb + k);
+                const float4 t = tab[c];
+                const double E = fp4_error16<WMSE>(v, w, t.x, t.y);
+                if (E < best || (E == best && c < cb)) {
+                    best = E;
+                    cb = c;
+                }
+            }
+#pragma unroll
+            for (int off = 8; off > 0; off >>= 1) {
+                const double E2 = __shfl_xor(best, off, 64);
+                const int c2 = __shfl_xor(cb, off, 64);
+                if (E2 < best || (E2 == best && c2 < cb)) {
+                    best = E2;
+                    cb = c2;
+                }
+            }
+            if (active && sub == 0) {
+                codes[blk] = fp4_encode16(v, tab[cb].y);
+                scales[blk] = (uint8_t)cb;
+            }
+        }
         __syncthreads();
         if (threadIdx.x == 0)
             qn = 0;
@@ -549,27 +555,23 @@ __global__ __launch_bounds__(kThreads) void mxfp4_quant(
 // dequantize and error
 // ---------------------------------------------------------------------------
 
-// decode one block's B values (before any un-rotation)
+// decode one block's B values (before any un-rotation): FP4 nibbles through
+// the hardware E2M1 decode (exact), times the block step D with one binary32
+// rounding, x_hat = fl32(+-v * D); IF4 INT4 blocks as q * fl32(D * fl32(6/7))
 template <int FMT, int B>
 __device__ __forceinline__ void decode_block(const uint32_t* wds, uint32_t sb, float S, float* o)
 {
+    float D;
     if constexpr (FMT == kMXFP4) {
-        const float D = (sb == 0xFFu) ? __builtin_nanf("")
-                        : (sb == 0u ? __uint_as_float(0x00400000u) : __uint_as_float(sb << 23));
-#pragma unroll
-        for (int i = 0; i < B; ++i) {
-            const uint32_t nib = (wds[i >> 3] >> (4 * (i & 7))) & 0xFu;
-            const float val = e2m1_value(nib & 7u) * D;
-            o[i] = (nib & 8u) ? -val : val;
-        }
+        D = (sb == 0xFFu) ? __builtin_nanf("")
+            : (sb == 0u ? __uint_as_float(0x00400000u) : __uint_as_float(sb << 23));
     } else {
         const uint32_t mag = sb & 0x7Fu;
         float s = (mag == 0x7Fu) ? __builtin_nanf("") : e4m3_value(mag);
-        const bool int4 = (FMT == kIF4) && (sb & 0x80u);
         if (FMT == kNVFP4 && (sb & 0x80u))
             s = -s;
-        const float D = s * S;
-        if (int4) {
+        D = s * S;
+        if (FMT == kIF4 && (sb & 0x80u)) {
             const float Di = D * kInt4Step;
 #pragma unroll
             for (int i = 0; i < B; ++i) {
@@ -577,14 +579,19 @@ __device__ __forceinline__ void decode_block(const uint32_t* wds, uint32_t sb, f
                 const int q = (nib & 8u) ? (int)nib - 16 : (int)nib;
                 o[i] = (float)q * Di;
             }
-        } else {
-#pragma unroll
-            for (int i = 0; i < B; ++i) {
-                const uint32_t nib = (wds[i >> 3] >> (4 * (i & 7))) & 0xFu;
-                const float val = e2m1_value(nib & 7u) * D;
-                o[i] = (nib & 8u) ? -val : val;
-            }
+            return;
         }
+    }
+#pragma unroll
+    for (int w = 0; w < B / 8; ++w) {
+        float q[8];
+        fp4_unpack2<0>(wds[w], q[0], q[1]);
+        fp4_unpack2<1>(wds[w], q[2], q[3]);
+        fp4_unpack2<2>(wds[w], q[4], q[5]);
+        fp4_unpack2<3>(wds[w], q[6], q[7]);
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+            o[8 * w + j] = q[j] * D;
     }
 }
 
@@ -620,10 +627,10 @@ __global__ __launch_bounds__(kThreads) void dequant(
 #pragma unroll
             for (int q = 0; q < B / 8; ++q) {
                 u32x4 t;
-                t.x = f32_to_bf16(o[8 * q + 0]) | (f32_to_bf16(o[8 * q + 1]) << 16);
-                t.y = f32_to_bf16(o[8 * q + 2]) | (f32_to_bf16(o[8 * q + 3]) << 16);
-                t.z = f32_to_bf16(o[8 * q + 4]) | (f32_to_bf16(o[8 * q + 5]) << 16);
-                t.w = f32_to_bf16(o[8 * q + 6]) | (f32_to_bf16(o[8 * q + 7]) << 16);
+                t.x = bf16_pair(o[8 * q + 0], o[8 * q + 1]);
+                t.y = bf16_pair(o[8 * q + 2], o[8 * q + 3]);
+                t.z = bf16_pair(o[8 * q + 4], o[8 * q + 5]);
+                t.w = bf16_pair(o[8 * q + 6], o[8 * q + 7]);
                 __builtin_nontemporal_store(t, p + q);
             }
         } else {
