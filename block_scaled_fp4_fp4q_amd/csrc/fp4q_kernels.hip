@@ -43,31 +43,38 @@ __device__ __forceinline__ void store_group_max(float m, float* partials)
     }
 }
 
-// un-rotated tensor: a flat, perfectly coalesced pass over 16-byte vectors
+// un-rotated tensor: a flat, perfectly coalesced pass over 16-byte vectors,
+// four loads in flight per lane
+template <bool BF16>
+__device__ __forceinline__ float vec_absmax(const uint4 w)
+{
+    if constexpr (BF16) {
+        const float a = __builtin_fmaxf(__builtin_fabsf(bf16_lo(w.x)), __builtin_fabsf(bf16_hi(w.x)));
+        const float b = __builtin_fmaxf(__builtin_fabsf(bf16_lo(w.y)), __builtin_fabsf(bf16_hi(w.y)));
+        const float c = __builtin_fmaxf(__builtin_fabsf(bf16_lo(w.z)), __builtin_fabsf(bf16_hi(w.z)));
+        const float d = __builtin_fmaxf(__builtin_fabsf(bf16_lo(w.w)), __builtin_fabsf(bf16_hi(w.w)));
+        return __builtin_fmaxf(__builtin_fmaxf(a, b), __builtin_fmaxf(c, d));
+    } else {
+        const float a = __builtin_fmaxf(__builtin_fabsf(__uint_as_float(w.x)), __builtin_fabsf(__uint_as_float(w.y)));
+        const float b = __builtin_fmaxf(__builtin_fabsf(__uint_as_float(w.z)), __builtin_fabsf(__uint_as_float(w.w)));
+        return __builtin_fmaxf(a, b);
+    }
+}
+
 template <bool BF16>
 __global__ __launch_bounds__(kThreads) void amax_flat(const uint4* __restrict__ x, int64_t nvec,
                                                       float* __restrict__ partials)
 {
     float m = 0.0f;
-    for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < nvec;
-         i += (int64_t)gridDim.x * kThreads) {
-        const uint4 w = x[i];
-        if constexpr (BF16) {
-            m = __builtin_fmaxf(m, __builtin_fabsf(bf16_lo(w.x)));
-            m = __builtin_fmaxf(m, __builtin_fabsf(bf16_hi(w.x)));
-            m = __builtin_fmaxf(m, __builtin_fabsf(bf16_lo(w.y)));
-            m = __builtin_fmaxf(m, __builtin_fabsf(bf16_hi(w.y)));
-            m = __builtin_fmaxf(m, __builtin_fabsf(bf16_lo(w.z)));
-            m = __builtin_fmaxf(m, __builtin_fabsf(bf16_hi(w.z)));
-            m = __builtin_fmaxf(m, __builtin_fabsf(bf16_lo(w.w)));
-            m = __builtin_fmaxf(m, __builtin_fabsf(bf16_hi(w.w)));
-        } else {
-            m = __builtin_fmaxf(m, __builtin_fabsf(__uint_as_float(w.x)));
-            m = __builtin_fmaxf(m, __builtin_fabsf(__uint_as_float(w.y)));
-            m = __builtin_fmaxf(m, __builtin_fabsf(__uint_as_float(w.z)));
-            m = __builtin_fmaxf(m, __builtin_fabsf(__uint_as_float(w.w)));
-        }
+    const int64_t stride = (int64_t)gridDim.x * kThreads;
+    int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+    for (; i + 3 * stride < nvec; i += 4 * stride) {
+        const uint4 w0 = x[i], w1 = x[i + stride], w2 = x[i + 2 * stride], w3 = x[i + 3 * stride];
+        m = __builtin_fmaxf(m, __builtin_fmaxf(__builtin_fmaxf(vec_absmax<BF16>(w0), vec_absmax<BF16>(w1)),
+                                               __builtin_fmaxf(vec_absmax<BF16>(w2), vec_absmax<BF16>(w3))));
     }
+    for (; i < nvec; i += stride)
+        m = __builtin_fmaxf(m, vec_absmax<BF16>(x[i]));
     store_group_max(m, partials);
 }
 
@@ -108,6 +115,35 @@ __global__ __launch_bounds__(1024) void finalize_scale(const float* __restrict__
         s = __builtin_fmaxf(s, 0x1p-117f);
         *S_out = (g == 0.0f) ? 1.0f : s;
     }
+}
+
+// The global scale seen by a quantize kernel: with npart > 0 every workgroup
+// reduces the partial maxima itself (a few KiB from L2, instead of a separate
+// one-workgroup launch) and workgroup 0 publishes S; with npart == 0 it is
+// read from *Sp (the caller supplied it).
+__device__ __forceinline__ float global_scale(const float* __restrict__ partials, int npart,
+                                              float* __restrict__ Sp)
+{
+    if (npart == 0)
+        return *Sp;
+    __shared__ float red[kThreads / 64];
+    float m = 0.0f;
+    for (int i = threadIdx.x; i < npart; i += kThreads)
+        m = __builtin_fmaxf(m, partials[i]);
+    m = wave_max(m);
+    if ((threadIdx.x & 63) == 0)
+        red[threadIdx.x >> 6] = m;
+    __syncthreads();
+    float g = red[0];
+#pragma unroll
+    for (int w = 1; w < kThreads / 64; ++w)
+        g = __builtin_fmaxf(g, red[w]);
+    float s = g / 1536.0f;
+    s = __builtin_fmaxf(s, 0x1p-117f);
+    s = (g == 0.0f) ? 1.0f : s;
+    if (blockIdx.x == 0 && threadIdx.x == 0)
+        *Sp = s;
+    return s;
 }
 
 // ---------------------------------------------------------------------------
@@ -184,10 +220,10 @@ __device__ __forceinline__ void load_weights16(const float* __restrict__ imp, in
 
 template <bool BF16, bool ROT>
 __global__ __launch_bounds__(kThreads) void nvfp4_absmax(
-    const void* __restrict__ x, int64_t nblocks, const float* __restrict__ Sp,
-    uint2* __restrict__ codes, uint8_t* __restrict__ scales)
+    const void* __restrict__ x, int64_t nblocks, const float* __restrict__ partials, int npart,
+    float* __restrict__ Sp, uint2* __restrict__ codes, uint8_t* __restrict__ scales)
 {
-    const float S = *Sp;
+    const float S = global_scale(partials, npart, Sp);
     const float S6 = 6.0f * S;
     for (int64_t blk = (int64_t)blockIdx.x * kThreads + threadIdx.x; blk < nblocks;
          blk += (int64_t)gridDim.x * kThreads) {
@@ -282,13 +318,39 @@ __device__ __forceinline__ void keep_best(float E, int c, float& e1, float& e2, 
     e1 = better ? E : e1;
 }
 
+// the whole window [LO, HI] known at compile time, every pattern sb+k normal
+// and finite, and every pair (k, k+8) an exact doubling: fully unrolled, no
+// clamps or masks (evaluation order differs from ascending k, which only
+// matters for exact ties, and those are never certified)
+template <bool WMSE, int LO, int HI>
+__device__ __forceinline__ void sweep_fixed(const float* v, const float* w, const float4* tab, int sb,
+                                            float& e1, float& e2, int& cb)
+{
+#pragma unroll
+    for (int k = LO; k <= HI; ++k) {
+        if (((k - LO) & 15) >= 8)
+            continue; // evaluated with its partner k-8
+        const int c = sb + k;
+        const float4 t = tab[c];
+        float F1, F2;
+        if (k + 8 <= HI) {
+            fp4_err32<WMSE, true>(v, w, t.y, F1, F2);
+            keep_best(F1 * t.z, c, e1, e2, cb);
+            keep_best(F2 * t.z, c + 8, e1, e2, cb);
+        } else {
+            fp4_err32<WMSE, false>(v, w, t.y, F1, F2);
+            keep_best(F1 * t.z, c, e1, e2, cb);
+        }
+    }
+}
+
 constexpr int kQueueCap = 1024; // fallback queue entries per workgroup (LDS)
 
-template <bool BF16, bool ROT, bool WMSE>
+template <bool BF16, bool ROT, bool WMSE, int WIN>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) void nvfp4_sweep(
     const void* __restrict__ x, int64_t nblocks, int64_t blocks_per_row,
-    const float* __restrict__ imp, const float* __restrict__ Sp, int lo, int hi,
-    uint2* __restrict__ codes, uint8_t* __restrict__ scales)
+    const float* __restrict__ imp, const float* __restrict__ partials, int npart,
+    float* __restrict__ Sp, int lo, int hi, uint2* __restrict__ codes, uint8_t* __restrict__ scales)
 {
     // per pattern: D = fl32(s S), r = fl32(1/D), fl32(D*D), and 1 when the
     // pattern eight steps up has exactly twice this step (so one product
@@ -296,7 +358,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
     __shared__ float4 tab[128];
     __shared__ int64_t queue[kQueueCap];
     __shared__ uint32_t qn;
-    const float S = *Sp;
+    const float S = global_scale(partials, npart, Sp);
     for (int c = threadIdx.x; c < 128; c += kThreads) {
         const float D = e4m3_value((uint32_t)(c < 0x7E ? c : 0x7E)) * S;
         const float D8 = e4m3_value((uint32_t)(c + 8 < 0x7E ? c + 8 : 0x7E)) * S;
@@ -306,6 +368,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
     if (threadIdx.x == 0)
         qn = 0;
     __syncthreads();
+    // every pair (c, c+8) with c in [8, 0x76] an exact doubling (true unless S
+    // pushes the steps to the ends of the binary32 range)
+    const bool pairs_exact = __syncthreads_and(threadIdx.x < 8 || threadIdx.x > 0x76 || tab[threadIdx.x].w != 0.0f);
+    constexpr int FLO = WIN == 1 ? -3 : -8, FHI = 7;
     const float S6 = 6.0f * S;
     constexpr float u = 0x1p-24f; // unit roundoff of binary32
     const int64_t stride = (int64_t)gridDim.x * kThreads;
@@ -398,6 +464,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
                 }
                 float e1 = __builtin_huge_valf(), e2 = __builtin_huge_valf();
                 int cb = 1;
+                const bool interior = WIN != 0 && pairs_exact && (int)sb + FLO >= 8 && (int)sb + FHI <= 0x7E;
+                if (WIN != 0 && __builtin_amdgcn_ballot_w64(!interior) == 0) {
+                    sweep_fixed<WMSE, FLO, FHI>(v, w, tab, (int)sb, e1, e2, cb);
+                } else
                 // offsets k and k+8 pair up in runs of eight; the rest are singles
                 for (int k = lo; k <= hi; ++k) {
                     if (((k - lo) & 15) >= 8)
@@ -470,10 +540,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
 template <bool BF16, bool ROT, bool WMSE>
 __global__ __launch_bounds__(kThreads) void if4_quant(
     const void* __restrict__ x, int64_t nblocks, int64_t blocks_per_row,
-    const float* __restrict__ imp, const float* __restrict__ Sp,
-    uint2* __restrict__ codes, uint8_t* __restrict__ scales)
+    const float* __restrict__ imp, const float* __restrict__ partials, int npart,
+    float* __restrict__ Sp, uint2* __restrict__ codes, uint8_t* __restrict__ scales)
 {
-    const float S = *Sp;
+    const float S = global_scale(partials, npart, Sp);
     const float S6 = 6.0f * S;
     for (int64_t blk = (int64_t)blockIdx.x * kThreads + threadIdx.x; blk < nblocks;
          blk += (int64_t)gridDim.x * kThreads) {
@@ -741,35 +811,47 @@ static int sweep_grid(K kernel, int64_t nb)
 }
 
 template <bool BF16, bool ROT>
-static void launch_nvfp4(const QuantArgs& a, int64_t nb, const float* Sp, int grid)
+static void launch_nvfp4(const QuantArgs& a, int64_t nb, const float* part, int npart, int grid)
 {
     const int64_t bpr = a.cols / 16;
+    float* Sp = a.global_scale;
     uint2* codes = reinterpret_cast<uint2*>(a.codes);
     if (a.rule == kAbsMax) {
         hipLaunchKernelGGL((nvfp4_absmax<BF16, ROT>), grid, kThreads, 0, a.stream,
-                           a.x, nb, Sp, codes, a.scales);
-    } else if (a.objective == kWMSE) {
-        auto k = nvfp4_sweep<BF16, ROT, true>;
-        hipLaunchKernelGGL(k, sweep_grid(k, nb), kThreads, 0, a.stream,
-                           a.x, nb, bpr, a.importance, Sp, a.lo, a.hi, codes, a.scales);
+                           a.x, nb, part, npart, Sp, codes, a.scales);
     } else {
-        auto k = nvfp4_sweep<BF16, ROT, false>;
-        hipLaunchKernelGGL(k, sweep_grid(k, nb), kThreads, 0, a.stream,
-                           a.x, nb, bpr, a.importance, Sp, a.lo, a.hi, codes, a.scales);
+        // the pages' two windows get a fully unrolled specialization
+        const int win = (a.lo == -3 && a.hi == 7) ? 1 : ((a.lo == -8 && a.hi == 7) ? 2 : 0);
+#define FP4Q_SWEEP(W, WI)                                                                      \
+    {                                                                                         \
+        auto k = nvfp4_sweep<BF16, ROT, W, WI>;                                               \
+        hipLaunchKernelGGL(k, sweep_grid(k, nb), kThreads, 0, a.stream, a.x, nb, bpr,           \
+                           a.importance, part, npart, Sp, a.lo, a.hi, codes, a.scales);       \
+    }
+        const bool wm = a.objective == kWMSE;
+        if (win == 1) {
+            if (wm) FP4Q_SWEEP(true, 1) else FP4Q_SWEEP(false, 1)
+        } else if (win == 2) {
+            if (wm) FP4Q_SWEEP(true, 2) else FP4Q_SWEEP(false, 2)
+        } else {
+            if (wm) FP4Q_SWEEP(true, 0) else FP4Q_SWEEP(false, 0)
+        }
+#undef FP4Q_SWEEP
     }
 }
 
 template <bool BF16, bool ROT>
-static void launch_if4(const QuantArgs& a, int64_t nb, const float* Sp, int grid)
+static void launch_if4(const QuantArgs& a, int64_t nb, const float* part, int npart, int grid)
 {
     const int64_t bpr = a.cols / 16;
+    float* Sp = a.global_scale;
     uint2* codes = reinterpret_cast<uint2*>(a.codes);
     if (a.objective == kWMSE)
         hipLaunchKernelGGL((if4_quant<BF16, ROT, true>), grid, kThreads, 0, a.stream,
-                           a.x, nb, bpr, a.importance, Sp, codes, a.scales);
+                           a.x, nb, bpr, a.importance, part, npart, Sp, codes, a.scales);
     else
         hipLaunchKernelGGL((if4_quant<BF16, ROT, false>), grid, kThreads, 0, a.stream,
-                           a.x, nb, bpr, a.importance, Sp, codes, a.scales);
+                           a.x, nb, bpr, a.importance, part, npart, Sp, codes, a.scales);
 }
 
 template <bool BF16>
@@ -791,32 +873,34 @@ hipError_t launch_quantize(const QuantArgs& a)
     const int B = (a.format == kMXFP4) ? 32 : 16;
     const int64_t nb = n / B;
     float* partials = reinterpret_cast<float*>(a.workspace);
-    const float* Sp = a.global_scale;
+    int npart = 0; // 0: the quantize kernel reads S from a.global_scale
     if (a.format != kMXFP4 && !a.global_scale_given) {
-        int groups = 0;
         if (n > 0) {
             const int64_t items = (a.rotate == 0) ? n * (a.bf16 ? 2 : 4) / 16 : nb;
-            groups = grid_for(items, kAmaxGroups);
+            npart = grid_for(items, kAmaxGroups);
             if (a.bf16)
-                launch_amax<true>(a, partials, groups);
+                launch_amax<true>(a, partials, npart);
             else
-                launch_amax<false>(a, partials, groups);
+                launch_amax<false>(a, partials, npart);
+        } else {
+            // nothing to reduce: S = 1 for an empty (all-zero) tensor
+            hipLaunchKernelGGL(finalize_scale, 1, 1024, 0, a.stream, partials, 0, a.global_scale);
         }
-        hipLaunchKernelGGL(finalize_scale, 1, 1024, 0, a.stream, partials, groups, a.global_scale);
     }
     if (nb > 0) {
         const int grid = grid_for(nb, kQuantGroupCap);
         const bool rot = a.rotate != 0;
+        const float* part = partials;
         if (a.format == kNVFP4) {
             if (a.bf16)
-                rot ? launch_nvfp4<true, true>(a, nb, Sp, grid) : launch_nvfp4<true, false>(a, nb, Sp, grid);
+                rot ? launch_nvfp4<true, true>(a, nb, part, npart, grid) : launch_nvfp4<true, false>(a, nb, part, npart, grid);
             else
-                rot ? launch_nvfp4<false, true>(a, nb, Sp, grid) : launch_nvfp4<false, false>(a, nb, Sp, grid);
+                rot ? launch_nvfp4<false, true>(a, nb, part, npart, grid) : launch_nvfp4<false, false>(a, nb, part, npart, grid);
         } else if (a.format == kIF4) {
             if (a.bf16)
-                rot ? launch_if4<true, true>(a, nb, Sp, grid) : launch_if4<true, false>(a, nb, Sp, grid);
+                rot ? launch_if4<true, true>(a, nb, part, npart, grid) : launch_if4<true, false>(a, nb, part, npart, grid);
             else
-                rot ? launch_if4<false, true>(a, nb, Sp, grid) : launch_if4<false, false>(a, nb, Sp, grid);
+                rot ? launch_if4<false, true>(a, nb, part, npart, grid) : launch_if4<false, false>(a, nb, part, npart, grid);
         } else {
             uint4* codes = reinterpret_cast<uint4*>(a.codes);
             if (a.bf16) {
