@@ -24,7 +24,14 @@
  *      carries the 6/7 factor, keep the lower MSE and record the choice in
  *      the scale's sign bit               [IF4, Methodology];
  *   9. MXFP4: one E8M0 power-of-two scale per 32 elements, no global scale
- *                                         [MR, Problem].
+ *                                         [MR, Problem];
+ *  10. extensions of the same search: Four Over Six (the block maximum onto
+ *      6 or onto 4, lower error kept) [IF4, Problem; SS, Problem definition];
+ *      a window of E8M0 exponents for MXFP4 [MR, Method 2: format-specific
+ *      scale search]; IF4 over a window of patterns, both grids per pattern;
+ *      and the FOCUS deploy-side encode, codes from S_q = S_dq * c with given
+ *      coefficients c per block or per 8 elements, S_dq stored [FOCUS,
+ *      Method 2 and 3].
  *
  * Readings taken where the pages are silent (each is listed in the design
  * notes): E2M1 and INT4 rounding is round-to-nearest with ties to the even
@@ -43,6 +50,7 @@
  */
 #include "fp4q_ref.h"
 
+#include <limits.h>
 #include <math.h>
 #include <pthread.h>
 #include <stdlib.h>
@@ -463,12 +471,64 @@ static void put_nibbles(uint8_t* codes, int64_t elem0, const uint8_t* nib, int B
         codes[(elem0 + i) / 2] = (uint8_t)((nib[i] & 0xF) | ((nib[i + 1] & 0xF) << 4));
 }
 
+/* keep the first least error among candidates tried in order; also the
+ * second least.  *cbest == NONE until the first candidate. */
+#define NONE INT_MIN
+static void consider(double E, int cand, double* best, double* second, int* cbest)
+{
+    if (*cbest == NONE || E < *best) {
+        if (*cbest != NONE)
+            *second = *best;
+        *best = E;
+        *cbest = cand;
+    } else if (E < *second) {
+        *second = E;
+    }
+}
+
+static int clamp_pattern(int c) { return c < 0x01 ? 0x01 : (c > 0x7E ? 0x7E : c); }
+
+/* MXFP4: E8M0 exponent of the OCP rule, floor(log2 max) - 2 in [-127, 127]
+ * ["Bridging the Gap ... Microscaling FP4", Problem: power-of-two scales] */
+static int mx_exponent(float a)
+{
+    int e = (a == 0.0f) ? -127 : floor_log2(a) - 2;
+    return e < -127 ? -127 : (e > 127 ? 127 : e);
+}
+
+/* MXFP4 encode of one block with exponent e; returns the block error */
+static double mx_block(const float* xb, int B, const float* w, int e, uint8_t* nib)
+{
+    float D = (float)ldexp(1.0, e);
+    float rr = (float)ldexp(1.0, -e);
+    double E = 0.0;
+    for (int i = 0; i < B; ++i) {
+        float av = fabsf(xb[i]);
+        int m = fp4q_ref_e2m1_round(av * rr);
+        float xh = fp4q_ref_e2m1_value(m) * D;
+        E = E + elem_err(av, xh, w, i);
+        if (nib)
+            nib[i] = (uint8_t)((signbit(xb[i]) ? 8 : 0) | m);
+    }
+    return E;
+}
+
+/* Four Over Six: the pattern that maps the block maximum onto 4 instead of 6
+ * [Adaptive Block-Scaled Data Types, Problem; ScaleSweep, Problem definition] */
+static int four_scale(const float* xb, int B, float S)
+{
+    float a = block_absmax(xb, B);
+    float s4 = 4.0f * S;
+    int sb = fp4q_ref_e4m3_round(a / s4);
+    return sb == 0 ? 1 : sb;
+}
+
 static void quant_rows(void* p, int64_t r0, int64_t r1)
 {
     quant_ctx* q = (quant_ctx*)p;
     const int B = q->block;
     const int64_t nbr = q->cols / B;
-    uint8_t nib[64], tmp[64];
+    uint8_t nib[64];
     for (int64_t r = r0; r < r1; ++r) {
         for (int64_t jb = 0; jb < nbr; ++jb) {
             int64_t e0 = r * q->cols + jb * B;
@@ -476,68 +536,78 @@ static void quant_rows(void* p, int64_t r0, int64_t r1)
             const float* xb = q->xr + e0;
             const float* w = (q->objective == REF_WMSE) ? q->imp + jb * B : NULL;
             double best = 0.0, second = INFINITY;
+            int cbest = NONE;
             uint8_t sbyte = 0;
             float a = block_absmax(xb, B);
 
             if (q->format == REF_MXFP4) {
-                int e = (a == 0.0f) ? -127 : floor_log2(a) - 2;
-                if (e < -127) e = -127;
-                if (e > 127) e = 127;
-                sbyte = (uint8_t)(e + 127);
-                float D = (float)ldexp(1.0, e);
-                float rr = (float)ldexp(1.0, -e);
-                best = 0.0;
-                for (int i = 0; i < B; ++i) {
-                    float av = fabsf(xb[i]);
-                    int m = fp4q_ref_e2m1_round(av * rr);
-                    float xh = fp4q_ref_e2m1_value(m) * D;
-                    best = best + elem_err(av, xh, NULL, i);
-                    nib[i] = (uint8_t)((signbit(xb[i]) ? 8 : 0) | m);
+                int e0x = mx_exponent(a);
+                if (q->rule == REF_SWEEP) {
+                    /* a window of E8M0 exponents around the OCP one, MSE or
+                     * WMSE argmin ["Bridging the Gap", Method 2: format-
+                     * specific scale search / scale fitting] */
+                    int eprev = 1000;
+                    for (int k = q->lo; k <= q->hi; ++k) {
+                        int e = e0x + k;
+                        e = e < -127 ? -127 : (e > 127 ? 127 : e);
+                        if (e == eprev)
+                            continue;
+                        eprev = e;
+                        consider(mx_block(xb, B, w, e, NULL), e, &best, &second, &cbest);
+                    }
+                } else {
+                    cbest = e0x;
+                    best = mx_block(xb, B, w, e0x, NULL);
                 }
+                best = mx_block(xb, B, w, cbest, nib);
+                sbyte = (uint8_t)(cbest + 127);
             } else if (a == 0.0f) {
                 /* all-zero block: scale byte 0, codes keep only the sign */
                 sbyte = 0;
                 for (int i = 0; i < B; ++i)
                     nib[i] = (uint8_t)(signbit(xb[i]) ? 8 : 0);
                 best = 0.0;
-                second = (q->format == REF_IF4 || q->rule == REF_SWEEP) ? 0.0 : INFINITY;
+                second = (q->format == REF_IF4 || q->rule != REF_ABSMAX) ? 0.0 : INFINITY;
             } else {
                 int sb = fp4q_ref_base_scale(xb, B, q->S);
                 if (q->format == REF_IF4) {
-                    double ef = fp4q_ref_nvfp4_block(xb, B, w, q->S, sb, nib);
-                    double ei = fp4q_ref_int4_block(xb, B, w, q->S, sb, tmp);
-                    if (ei < ef) {
-                        memcpy(nib, tmp, (size_t)B);
-                        sbyte = (uint8_t)(sb | 0x80);
-                        best = ei;
-                        second = ef;
-                    } else {
-                        sbyte = (uint8_t)sb;
-                        best = ef;
-                        second = ei;
-                    }
-                } else if (q->rule == REF_ABSMAX) {
-                    sbyte = (uint8_t)sb;
-                    best = fp4q_ref_nvfp4_block(xb, B, w, q->S, sb, nib);
-                } else {
-                    int cbest = -1, cprev = -1;
-                    for (int k = q->lo; k <= q->hi; ++k) {
-                        /* patterns past either end of [0x01, 0x7E] stand for the
-                         * end pattern itself; each pattern is tried once */
-                        int c = sb + k;
-                        c = c < 0x01 ? 0x01 : (c > 0x7E ? 0x7E : c);
+                    /* per pattern: FP4 first, then INT4 (indicator bit 7) */
+                    int lo = q->rule == REF_SWEEP ? q->lo : 0;
+                    int hi = q->rule == REF_SWEEP ? q->hi : 0;
+                    int cprev = -1;
+                    for (int k = lo; k <= hi; ++k) {
+                        int c = clamp_pattern(sb + k);
                         if (c == cprev)
                             continue;
                         cprev = c;
-                        double E = fp4q_ref_nvfp4_block(xb, B, w, q->S, c, NULL);
-                        if (cbest < 0 || E < best) {
-                            if (cbest >= 0)
-                                second = best;
-                            best = E;
-                            cbest = c;
-                        } else if (E < second) {
-                            second = E;
-                        }
+                        consider(fp4q_ref_nvfp4_block(xb, B, w, q->S, c, NULL), c, &best, &second, &cbest);
+                        consider(fp4q_ref_int4_block(xb, B, w, q->S, c, NULL), c | 0x80, &best, &second, &cbest);
+                    }
+                    if (cbest & 0x80)
+                        fp4q_ref_int4_block(xb, B, w, q->S, cbest & 0x7F, nib);
+                    else
+                        fp4q_ref_nvfp4_block(xb, B, w, q->S, cbest, nib);
+                    sbyte = (uint8_t)cbest;
+                } else if (q->rule == REF_ABSMAX) {
+                    sbyte = (uint8_t)sb;
+                    best = fp4q_ref_nvfp4_block(xb, B, w, q->S, sb, nib);
+                } else if (q->rule == REF_FOUR_SIX) {
+                    int s4 = four_scale(xb, B, q->S);
+                    consider(fp4q_ref_nvfp4_block(xb, B, w, q->S, sb, NULL), sb, &best, &second, &cbest);
+                    if (s4 != sb)
+                        consider(fp4q_ref_nvfp4_block(xb, B, w, q->S, s4, NULL), s4, &best, &second, &cbest);
+                    sbyte = (uint8_t)cbest;
+                    fp4q_ref_nvfp4_block(xb, B, w, q->S, cbest, nib);
+                } else {
+                    int cprev = -1;
+                    for (int k = q->lo; k <= q->hi; ++k) {
+                        /* patterns past either end of [0x01, 0x7E] stand for the
+                         * end pattern itself; each pattern is tried once */
+                        int c = clamp_pattern(sb + k);
+                        if (c == cprev)
+                            continue;
+                        cprev = c;
+                        consider(fp4q_ref_nvfp4_block(xb, B, w, q->S, c, NULL), c, &best, &second, &cbest);
                     }
                     sbyte = (uint8_t)cbest;
                     fp4q_ref_nvfp4_block(xb, B, w, q->S, cbest, nib);
@@ -611,8 +681,12 @@ int fp4q_ref_quantize(int format, int block, int scale_rule, int objective,
         return -1;
     if (objective == REF_WMSE && !importance)
         return -1;
-    if (scale_rule == REF_SWEEP && (format != REF_NVFP4 || sweep_lo > sweep_hi))
+    if (scale_rule == REF_SWEEP && sweep_lo > sweep_hi)
+        return -2;
+    if (scale_rule == REF_FOUR_SIX && format != REF_NVFP4)
         return -4;
+    if (scale_rule < REF_ABSMAX || scale_rule > REF_FOUR_SIX)
+        return -2;
 
     int64_t n = rows * cols;
     float* xr = (float*)malloc(sizeof(float) * (size_t)(n > 0 ? n : 1));
@@ -641,6 +715,108 @@ int fp4q_ref_quantize(int format, int block, int scale_rule, int objective,
     quant_ctx q = {format, block, scale_rule, objective, sweep_lo, sweep_hi,
                    xr, cols, importance, S, codes, scales, best_err, second_err};
     parallel_rows(rows, nthreads, quant_rows, &q);
+    free(xr);
+    return 0;
+}
+
+/* ------------------------------------------------------------------------ */
+/* FOCUS deploy-side encode                                                 */
+/* ------------------------------------------------------------------------ */
+
+/* Codes from the relaxed quantization scale S_q = S_dq * c while the stored
+ * (dequantization) scale stays S_dq [FOCUS, Method 2 "coupled-relaxation
+ * scaling": S_q = S_dq c_i; Method 3 "dual-granularity scaling": one c_k per
+ * sub-block of 8 with S_dq shared by the block].  S_dq is the AbsMax scale
+ * (NVFP4: E4M3 of max/(6S); MXFP4: the OCP exponent) or, when scales_given,
+ * the caller's bytes.  Per element: D_q = fl(D c), r_q = fl(1/D_q),
+ * code = E2M1(fl(|x| r_q)); a block whose step D is 0 keeps only signs. */
+typedef struct {
+    int format, block, group, scales_given;
+    const float* xr;
+    int64_t cols;
+    const float* coef;
+    float S;
+    uint8_t* codes;
+    uint8_t* scales;
+} relax_ctx;
+
+static void relax_rows(void* p, int64_t r0, int64_t r1)
+{
+    relax_ctx* q = (relax_ctx*)p;
+    const int B = q->block;
+    const int64_t nbr = q->cols / B, ngr = q->cols / q->group;
+    uint8_t nib[64];
+    for (int64_t r = r0; r < r1; ++r) {
+        for (int64_t jb = 0; jb < nbr; ++jb) {
+            int64_t e0 = r * q->cols + jb * B;
+            int64_t bi = r * nbr + jb;
+            const float* xb = q->xr + e0;
+            int byte;
+            float D;
+            if (q->scales_given) {
+                byte = q->scales[bi];
+                D = (q->format == REF_MXFP4) ? fp4q_ref_e8m0_value(byte)
+                                             : fp4q_ref_e4m3_value(byte) * q->S;
+            } else if (q->format == REF_MXFP4) {
+                int e = mx_exponent(block_absmax(xb, B));
+                byte = e + 127;
+                D = (float)ldexp(1.0, e);
+            } else {
+                byte = fp4q_ref_base_scale(xb, B, q->S);
+                D = byte ? fp4q_ref_e4m3_value(byte) * q->S : 0.0f;
+            }
+            for (int i = 0; i < B; ++i) {
+                int m = 0;
+                if (D != 0.0f) {
+                    float c = q->coef[r * ngr + (jb * B + i) / q->group];
+                    float Dq = D * c;
+                    float rq = 1.0f / Dq;
+                    m = fp4q_ref_e2m1_round(fabsf(xb[i]) * rq);
+                }
+                nib[i] = (uint8_t)((signbit(xb[i]) ? 8 : 0) | m);
+            }
+            put_nibbles(q->codes, e0, nib, B);
+            if (!q->scales_given)
+                q->scales[bi] = (uint8_t)byte;
+        }
+    }
+}
+
+int fp4q_ref_quantize_relaxed(int format, int block, int global_scale_given,
+                              const void* x, int x_dtype, int64_t rows, int64_t cols,
+                              const float* coef, int group, int scales_given,
+                              uint8_t* codes, uint8_t* scales, float* global_scale,
+                              int nthreads)
+{
+    int rc = check_common(format, block, 0, rows, cols);
+    if (rc)
+        return rc;
+    if (format == REF_IF4)
+        return -4;
+    if (group != 8 && group != block)
+        return -2;
+    if (!x || !coef || !codes || !scales || (format != REF_MXFP4 && !global_scale))
+        return -1;
+    int64_t n = rows * cols;
+    float* xr = (float*)malloc(sizeof(float) * (size_t)(n > 0 ? n : 1));
+    if (!xr)
+        return -6;
+    fp4q_ref_prepare(x, x_dtype, rows, cols, 0, xr, nthreads);
+    float S = 1.0f;
+    if (format != REF_MXFP4) {
+        if (global_scale_given) {
+            S = *global_scale;
+        } else {
+            float g = 0.0f;
+            for (int64_t k = 0; k < n; ++k)
+                if (fabsf(xr[k]) > g)
+                    g = fabsf(xr[k]);
+            S = fp4q_ref_global_scale(g);
+            *global_scale = S;
+        }
+    }
+    relax_ctx q = {format, block, group, scales_given, xr, cols, coef, S, codes, scales};
+    parallel_rows(rows, nthreads, relax_rows, &q);
     free(xr);
     return 0;
 }

@@ -34,7 +34,7 @@ extern "C" {
 /* numeric codes used by the oracle's own entry points */
 enum { REF_NVFP4 = 0, REF_MXFP4 = 1, REF_IF4 = 2 };
 enum { REF_F32 = 0, REF_BF16 = 1 };
-enum { REF_ABSMAX = 0, REF_SWEEP = 1 };
+enum { REF_ABSMAX = 0, REF_SWEEP = 1, REF_FOUR_SIX = 2 };
 enum { REF_MSE = 0, REF_WMSE = 1 };
 
 /* ---- element / scale formats ------------------------------------------ */
@@ -85,6 +85,15 @@ int fp4q_ref_quantize(int format, int block, int scale_rule, int objective,
                       const float* importance,
                       uint8_t* codes, uint8_t* scales, float* global_scale,
                       double* best_err, double* second_err, int nthreads);
+
+/* FOCUS deploy-side encode: codes from S_q = S_dq * c (c per `group`
+ * elements, group 8 or the block), S_dq stored (AbsMax rule, or read from
+ * `scales` when scales_given).  coef: fp32 [rows, cols/group]. */
+int fp4q_ref_quantize_relaxed(int format, int block, int global_scale_given,
+                              const void* x, int x_dtype, int64_t rows, int64_t cols,
+                              const float* coef, int group, int scales_given,
+                              uint8_t* codes, uint8_t* scales, float* global_scale,
+                              int nthreads);
 
 int fp4q_ref_dequantize(int format, int block, const uint8_t* codes,
                         const uint8_t* scales, const float* global_scale,

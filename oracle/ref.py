@@ -12,7 +12,7 @@ from . import build as _build
 
 NVFP4, MXFP4, IF4 = 0, 1, 2
 F32, BF16 = 0, 1
-ABSMAX, SWEEP = 0, 1
+ABSMAX, SWEEP, FOUR_SIX = 0, 1, 2
 MSE, WMSE = 0, 1
 
 _lib = None
@@ -47,6 +47,7 @@ def lib():
             "fp4q_ref_quantize": (i, [i, i, i, i, i, i, i, i, vp, i, i64, i64,
                                       vp, vp, vp, vp, vp, vp, i]),
             "fp4q_ref_dequantize": (i, [i, i, vp, vp, vp, i64, i64, i, vp, i, i]),
+            "fp4q_ref_quantize_relaxed": (i, [i, i, i, vp, i, i64, i64, vp, i, i, vp, vp, vp, i]),
             "fp4q_ref_error": (i, [i, i, i, vp, i, i64, i64, vp, vp, vp, vp, vp, i]),
         }
         for name, (res, args) in sig.items():
@@ -73,7 +74,9 @@ def block_size(fmt):
     return 32 if fmt == MXFP4 else 16
 
 
-def default_window(objective):
+def default_window(objective, fmt=NVFP4):
+    if fmt == MXFP4:
+        return (0, 1)
     return (-8, 7) if objective == WMSE else (-3, 7)
 
 
@@ -83,7 +86,7 @@ def quantize(x, fmt=NVFP4, rule=ABSMAX, objective=MSE, window=None, rotate=0,
     x = np.ascontiguousarray(x)
     rows, cols = x.shape
     B = block_size(fmt)
-    lo, hi = window if window is not None else default_window(objective)
+    lo, hi = window if window is not None else default_window(objective, fmt)
     nb = rows * cols // B
     codes = np.zeros(rows * cols // 2, np.uint8)
     scales = np.zeros(nb, np.uint8)
@@ -102,6 +105,24 @@ def quantize(x, fmt=NVFP4, rule=ABSMAX, objective=MSE, window=None, rotate=0,
         out["best"] = best
         out["second"] = second
     return out
+
+
+def quantize_relaxed(x, coef, group, fmt=NVFP4, global_scale=None, scales=None, nthreads=0):
+    """FOCUS deploy-side encode with given coefficients (fp32 [rows, cols/group])."""
+    x = np.ascontiguousarray(x)
+    rows, cols = x.shape
+    B = block_size(fmt)
+    codes = np.zeros(rows * cols // 2, np.uint8)
+    given = scales is not None
+    sc = np.array(scales, np.uint8).copy() if given else np.zeros(rows * cols // B, np.uint8)
+    gs = np.array([global_scale if global_scale is not None else 0.0], np.float32)
+    coef = np.ascontiguousarray(coef, np.float32)
+    rc = lib().fp4q_ref_quantize_relaxed(fmt, B, int(global_scale is not None), _p(x),
+                                         _dtype_code(x), rows, cols, _p(coef), group, int(given),
+                                         _p(codes), _p(sc), _p(gs), nthreads)
+    if rc != 0:
+        raise ValueError(f"fp4q_ref_quantize_relaxed failed: {rc}")
+    return {"codes": codes, "scales": sc, "S": float(gs[0])}
 
 
 def dequantize(codes, scales, S, rows, cols, fmt=NVFP4, unrotate=0, out_dtype=F32,

@@ -176,3 +176,90 @@ def hadamard(n):
 def pack(nibbles):
     nib = list(nibbles)
     return bytes((nib[i] & 0xF) | ((nib[i + 1] & 0xF) << 4) for i in range(0, len(nib), 2))
+
+
+def quantize_block_foursix(xb, S, w=None):
+    """Four Over Six: the max onto 6 (AbsMax) or onto 4, lower exact error,
+    a tie keeps 6."""
+    a = max(abs(f32(v)) for v in xb)
+    if a == 0:
+        return 0, [(8 if np.signbit(f32(v)) else 0) for v in xb], Fr(0)
+    s6 = base_byte(a, S)
+    t4 = f32(a) / (f32(4.0) * f32(S))
+    s4 = max(nearest(Fr(float(t4)), E4M3), 1)
+    e6, n6 = encode_fp4(xb, S, s6, w)
+    e4, n4 = encode_fp4(xb, S, s4, w)
+    if e4 < e6:
+        return s4, n4, e4
+    return s6, n6, e6
+
+
+def mx_encode(xb, e, w=None):
+    D = Fr(2) ** e
+    nib, err = [], Fr(0)
+    for i, x in enumerate(xb):
+        x = f32(x)
+        av = Fr(float(abs(x)))
+        m = nearest(av / D, E2M1)
+        t = (av - E2M1[m] * D) ** 2
+        if w is not None:
+            t *= Fr(float(f32(w[i])))
+        err += t
+        nib.append((8 if np.signbit(x) else 0) | m)
+    return err, nib
+
+
+def quantize_block_mx_sweep(xb, window, w=None):
+    e0 = quantize_block_mxfp4(xb)[0] - 127
+    errs = {}
+    for k in range(window[0], window[1] + 1):
+        e = min(127, max(-127, e0 + k))
+        if e not in errs:
+            errs[e] = mx_encode(xb, e, w)[0]
+    eb = min(errs, key=lambda e: (errs[e], e))
+    err, nib = mx_encode(xb, eb, w)
+    return eb + 127, nib, err
+
+
+def quantize_block_if4_sweep(xb, S, window, w=None):
+    a = max(abs(f32(v)) for v in xb)
+    if a == 0:
+        return 0, [(8 if np.signbit(f32(v)) else 0) for v in xb], Fr(0)
+    sb = base_byte(a, S)
+    opts = []
+    seen = set()
+    for k in range(window[0], window[1] + 1):
+        c = min(0x7E, max(0x01, sb + k))
+        if c in seen:
+            continue
+        seen.add(c)
+        ef, nf = encode_fp4(xb, S, c, w)
+        ei, ni = encode_int4(xb, S, c, w)
+        opts.append((ef, c, c, nf))
+        opts.append((ei, c + 0.5, c | 0x80, ni))   # INT4 after FP4 of the same pattern
+    e, _, byte, nib = min(opts, key=lambda o: (o[0], o[1]))
+    return byte, nib, e
+
+
+def relaxed_block(xb, S, coefs, byte=None, fmt="nvfp4"):
+    """FOCUS deploy encode of one block: codes from D*c, S_dq (byte) stored."""
+    a = max(abs(f32(v)) for v in xb)
+    if byte is None:
+        if fmt == "mxfp4":
+            byte = quantize_block_mxfp4(xb)[0]
+        else:
+            byte = 0 if a == 0 else base_byte(a, S)
+    if fmt == "mxfp4":
+        D = f32(2.0 ** (byte - 127))
+    else:
+        D = f32(float(E4M3[byte])) * f32(S) if byte else f32(0)
+    nib = []
+    for x, c in zip(xb, coefs):
+        x = f32(x)
+        m = 0
+        if D != 0:
+            Dq = D * f32(c)
+            rq = f32(1.0) / Dq
+            m = nearest(Fr(float(abs(x) * rq)), E2M1)
+        nib.append((8 if np.signbit(x) else 0) | m)
+    return byte, nib
