@@ -15,15 +15,15 @@ LIB_PATH = os.path.join(_HERE, "libfp4q.so")
 
 FP4Q_NVFP4, FP4Q_MXFP4, FP4Q_IF4 = 0, 1, 2
 FP4Q_F32, FP4Q_BF16 = 0, 1
-FP4Q_SCALE_ABSMAX, FP4Q_SCALE_SWEEP = 0, 1
+FP4Q_SCALE_ABSMAX, FP4Q_SCALE_SWEEP, FP4Q_SCALE_FOUR_OVER_SIX = 0, 1, 2
 FP4Q_OBJ_MSE, FP4Q_OBJ_WMSE = 0, 1
 
 STATUS = {0: "FP4Q_OK", -1: "FP4Q_E_NULL", -2: "FP4Q_E_ARG", -3: "FP4Q_E_SHAPE",
           -4: "FP4Q_E_UNSUPPORTED", -5: "FP4Q_E_HIP", -6: "FP4Q_E_ALIGN"}
 
 # every symbol include/fp4q.h declares
-EXPORTS = ("fp4q_workspace_bytes", "fp4q_quantize", "fp4q_dequantize", "fp4q_error",
-           "fp4q_status_string", "fp4q_abi_version")
+EXPORTS = ("fp4q_workspace_bytes", "fp4q_quantize", "fp4q_quantize_relaxed", "fp4q_dequantize",
+           "fp4q_error", "fp4q_status_string", "fp4q_abi_version")
 
 
 class fp4q_spec(C.Structure):
@@ -55,6 +55,9 @@ def _lib_handle():
         L.fp4q_workspace_bytes.argtypes = [sp, i64, i64]
         L.fp4q_quantize.restype = C.c_int
         L.fp4q_quantize.argtypes = [sp, vp, i32, i64, i64, vp, vp, vp, vp, vp, sz, vp]
+        L.fp4q_quantize_relaxed.restype = C.c_int
+        L.fp4q_quantize_relaxed.argtypes = [sp, vp, i32, i64, i64, vp, i32, i32, vp, vp, vp, vp,
+                                            sz, vp]
         L.fp4q_dequantize.restype = C.c_int
         L.fp4q_dequantize.argtypes = [sp, vp, vp, vp, i64, i64, i32, vp, i32, vp]
         L.fp4q_error.restype = C.c_int
@@ -102,7 +105,11 @@ def _check(fn, st):
 def make_spec(format=FP4Q_NVFP4, scale_rule=FP4Q_SCALE_ABSMAX, objective=FP4Q_OBJ_MSE,
               window=None, rotate=0, global_scale_given=False):
     block = 32 if format == FP4Q_MXFP4 else 16
-    lo, hi = window if window is not None else ((-8, 7) if objective == FP4Q_OBJ_WMSE else (-3, 7))
+    if window is None:
+        # E8M0: the OCP exponent and the next one up; E4M3: the pages' windows
+        window = (0, 1) if format == FP4Q_MXFP4 else \
+            ((-8, 7) if objective == FP4Q_OBJ_WMSE else (-3, 7))
+    lo, hi = window
     return fp4q_spec(format, block, scale_rule, objective, lo, hi, rotate, int(global_scale_given))
 
 
@@ -130,6 +137,17 @@ def fp4q_quantize(spec, x, importance, codes, scales, global_scale, workspace, s
                                      _ptr(global_scale), _ptr(workspace), workspace.numel(),
                                      _stream(stream))
     _check("fp4q_quantize", st)
+
+
+def fp4q_quantize_relaxed(spec, x, coef, coef_group, scales_given, codes, scales, global_scale,
+                          workspace, stream=None):
+    x2 = _as_2d(x)
+    rows, cols = x2.shape
+    st = _lib_handle().fp4q_quantize_relaxed(C.byref(spec), _ptr(x2), _dtype_code(x2), rows, cols,
+                                             _ptr(coef), coef_group, int(scales_given), _ptr(codes),
+                                             _ptr(scales), _ptr(global_scale), _ptr(workspace),
+                                             workspace.numel(), _stream(stream))
+    _check("fp4q_quantize_relaxed", st)
 
 
 def fp4q_dequantize(spec, codes, scales, global_scale, rows, cols, unrotate, y, stream=None):
@@ -180,6 +198,27 @@ def quantize(x, format=FP4Q_NVFP4, scale_rule=FP4Q_SCALE_ABSMAX, objective=FP4Q_
     ws = workspace if workspace is not None else alloc_workspace(spec, rows, cols, dev)
     fp4q_quantize(spec, x2, importance, codes, scales, gs, ws, stream)
     return codes, scales, gs
+
+
+def quantize_relaxed(x, coef, coef_group, format=FP4Q_NVFP4, scales=None, global_scale=None,
+                     workspace=None, stream=None):
+    """FOCUS deploy encode.  coef: float32 [rows, cols/coef_group] on the
+    device; scales: given S_dq bytes, or None to compute the AbsMax ones.
+    Returns (codes, scales, global_scale)."""
+    spec = make_spec(format, global_scale_given=global_scale is not None)
+    x2 = _as_2d(x)
+    rows, cols = x2.shape
+    dev = x.device
+    codes = torch.empty(rows * cols // 2, dtype=torch.uint8, device=dev)
+    given = scales is not None
+    sc = scales if given else torch.empty(rows * cols // spec.block, dtype=torch.uint8, device=dev)
+    if global_scale is None:
+        gs = torch.empty(1, dtype=torch.float32, device=dev)
+    else:
+        gs = torch.as_tensor(global_scale, dtype=torch.float32, device=dev).reshape(1).clone()
+    ws = workspace if workspace is not None else alloc_workspace(spec, rows, cols, dev)
+    fp4q_quantize_relaxed(spec, x2, coef, coef_group, given, codes, sc, gs, ws, stream)
+    return codes, sc, gs
 
 
 def dequantize(codes, scales, global_scale, rows, cols, format=FP4Q_NVFP4, unrotate=0,

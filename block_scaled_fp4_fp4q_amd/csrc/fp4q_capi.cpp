@@ -29,18 +29,18 @@ fp4q_status check_spec(const fp4q_spec* s, bool for_quantize)
         return FP4Q_E_ARG;
     if (!for_quantize)
         return FP4Q_OK;
-    if (s->scale_rule != FP4Q_SCALE_ABSMAX && s->scale_rule != FP4Q_SCALE_SWEEP)
+    if (s->scale_rule != FP4Q_SCALE_ABSMAX && s->scale_rule != FP4Q_SCALE_SWEEP &&
+        s->scale_rule != FP4Q_SCALE_FOUR_OVER_SIX)
         return FP4Q_E_ARG;
     if (s->objective != FP4Q_OBJ_MSE && s->objective != FP4Q_OBJ_WMSE)
         return FP4Q_E_ARG;
     if (s->global_scale_given != 0 && s->global_scale_given != 1)
         return FP4Q_E_ARG;
-    if (s->scale_rule == FP4Q_SCALE_SWEEP) {
-        if (s->format != FP4Q_NVFP4)
-            return FP4Q_E_UNSUPPORTED;
-        if (s->sweep_lo > s->sweep_hi || s->sweep_lo < -126 || s->sweep_hi > 126)
-            return FP4Q_E_ARG;
-    }
+    if (s->scale_rule == FP4Q_SCALE_FOUR_OVER_SIX && s->format != FP4Q_NVFP4)
+        return FP4Q_E_UNSUPPORTED;
+    if (s->scale_rule == FP4Q_SCALE_SWEEP &&
+        (s->sweep_lo > s->sweep_hi || s->sweep_lo < -126 || s->sweep_hi > 126))
+        return FP4Q_E_ARG;
     return FP4Q_OK;
 }
 
@@ -70,7 +70,7 @@ const char* fp4q_status_string(fp4q_status s)
     case FP4Q_E_NULL: return "a required pointer is NULL";
     case FP4Q_E_ARG: return "invalid argument (enum, window, rotation or workspace size)";
     case FP4Q_E_SHAPE: return "invalid shape (negative size, or cols not a multiple of the block)";
-    case FP4Q_E_UNSUPPORTED: return "unsupported combination (block size, or ScaleSweep outside NVFP4)";
+    case FP4Q_E_UNSUPPORTED: return "unsupported combination (block size, Four Over Six outside NVFP4, relaxed IF4 or rotation)";
     case FP4Q_E_HIP: return "the HIP runtime refused a launch or copy";
     case FP4Q_E_ALIGN: return "a tensor pointer is not aligned as required";
     }
@@ -96,8 +96,9 @@ fp4q_status fp4q_quantize(const fp4q_spec* spec, const void* x, int32_t x_dtype,
     if (!valid_dtype(x_dtype))
         return FP4Q_E_ARG;
     const bool has_gs = spec->format != FP4Q_MXFP4;
+    // the weights matter wherever a block error decides between candidates
     const bool wants_imp = spec->objective == FP4Q_OBJ_WMSE &&
-                           (spec->scale_rule == FP4Q_SCALE_SWEEP || spec->format == FP4Q_IF4);
+                           (spec->scale_rule != FP4Q_SCALE_ABSMAX || spec->format == FP4Q_IF4);
     const bool empty = rows == 0 || cols == 0; // tensor pointers may then be NULL
     if ((!empty && (!x || !codes || !scales)) || !workspace || (has_gs && !global_scale) ||
         (wants_imp && !empty && !importance))
@@ -110,7 +111,8 @@ fp4q_status fp4q_quantize(const fp4q_spec* spec, const void* x, int32_t x_dtype,
 
     fp4q::QuantArgs a{};
     a.format = spec->format;
-    a.rule = spec->scale_rule;
+    a.rule = spec->scale_rule == FP4Q_SCALE_SWEEP ? fp4q::kSweep
+           : spec->scale_rule == FP4Q_SCALE_FOUR_OVER_SIX ? fp4q::kFourSix : fp4q::kAbsMax;
     a.objective = wants_imp ? fp4q::kWMSE : fp4q::kMSE;
     a.lo = spec->sweep_lo;
     a.hi = spec->sweep_hi;
@@ -127,6 +129,49 @@ fp4q_status fp4q_quantize(const fp4q_spec* spec, const void* x, int32_t x_dtype,
     a.workspace = workspace;
     a.stream = static_cast<hipStream_t>(stream);
     return fp4q::launch_quantize(a) == hipSuccess ? FP4Q_OK : FP4Q_E_HIP;
+}
+
+fp4q_status fp4q_quantize_relaxed(const fp4q_spec* spec, const void* x, int32_t x_dtype,
+                                  int64_t rows, int64_t cols, const float* coef, int32_t coef_group,
+                                  int32_t scales_given, uint8_t* codes, uint8_t* scales,
+                                  float* global_scale, void* workspace, size_t ws_bytes, void* stream)
+{
+    fp4q_status st = check_spec(spec, false);
+    if (st != FP4Q_OK)
+        return st;
+    if ((st = check_shape(rows, cols, spec->block)) != FP4Q_OK)
+        return st;
+    if (spec->format == FP4Q_IF4 || spec->rotate != 0)
+        return FP4Q_E_UNSUPPORTED;
+    if (!valid_dtype(x_dtype) || (coef_group != 8 && coef_group != spec->block) ||
+        (scales_given != 0 && scales_given != 1) ||
+        (spec->global_scale_given != 0 && spec->global_scale_given != 1))
+        return FP4Q_E_ARG;
+    const bool has_gs = spec->format != FP4Q_MXFP4;
+    const bool empty = rows == 0 || cols == 0;
+    if ((!empty && (!x || !coef || !codes || !scales)) || !workspace || (has_gs && !global_scale))
+        return FP4Q_E_NULL;
+    if (ws_bytes < fp4q::kWorkspaceBytes)
+        return FP4Q_E_ARG;
+    if (!aligned(x, 16) || !aligned(codes, spec->block == 32 ? 16 : 8) || !aligned(coef, 4) ||
+        !aligned(workspace, 256) || (has_gs && !aligned(global_scale, 4)))
+        return FP4Q_E_ALIGN;
+    fp4q::RelaxArgs a{};
+    a.format = spec->format;
+    a.group = coef_group;
+    a.global_scale_given = spec->global_scale_given != 0;
+    a.scales_given = scales_given != 0;
+    a.bf16 = x_dtype == FP4Q_BF16;
+    a.x = x;
+    a.rows = rows;
+    a.cols = cols;
+    a.coef = coef;
+    a.codes = codes;
+    a.scales = scales;
+    a.global_scale = global_scale;
+    a.workspace = workspace;
+    a.stream = static_cast<hipStream_t>(stream);
+    return fp4q::launch_quantize_relaxed(a) == hipSuccess ? FP4Q_OK : FP4Q_E_HIP;
 }
 
 fp4q_status fp4q_dequantize(const fp4q_spec* spec, const uint8_t* codes, const uint8_t* scales,

@@ -621,6 +621,270 @@ __global__ __launch_bounds__(kThreads) void mxfp4_quant(
     }
 }
 
+// 2^k as binary32, exact for k in [-149, 127]
+__device__ __forceinline__ float pow2f(int k)
+{
+    return k >= -126 ? __uint_as_float((uint32_t)(k + 127) << 23) : __uint_as_float(1u << (k + 149));
+}
+
+// OCP E8M0 exponent of a block maximum, clamped to [-127, 127]
+__device__ __forceinline__ int mx_exponent(float a)
+{
+    const int e = (a == 0.0f) ? -127 : floor_log2_f32(a) - 2;
+    return e < -127 ? -127 : (e > 127 ? 127 : e);
+}
+
+// the 32 nibbles of E2M1(|v| 2^-e) with signs
+__device__ __forceinline__ uint4 mx_encode32(const float* v, int e)
+{
+    const float r = pow2f(-e);
+    uint32_t wds[4] = {0, 0, 0, 0};
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+        const uint32_t sgn = __float_as_uint(v[i]) >> 31;
+        const float q = e2m1_q(__builtin_fabsf(v[i]) * r);
+        wds[i >> 3] |= ((sgn << 3) | e2m1_code(q)) << (4 * (i & 7));
+    }
+    return make_uint4(wds[0], wds[1], wds[2], wds[3]);
+}
+
+// binary64 block error of the MXFP4 encoding with exponent e
+template <bool WMSE>
+__device__ __forceinline__ double mx_error32(const float* v, const float* w, int e)
+{
+    const float D = pow2f(e), r = pow2f(-e);
+    double E = 0.0;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+        const float a = __builtin_fabsf(v[i]);
+        const float xh = e2m1_q(a * r) * D;
+        const double d = (double)a - (double)xh;
+        double t = d * d;
+        if constexpr (WMSE)
+            t = (double)w[i] * t;
+        E = E + t;
+    }
+    return E;
+}
+
+__device__ __forceinline__ void load_weights32(const float* __restrict__ imp, int64_t col0, float* w)
+{
+    load_weights16(imp, col0, w);
+    load_weights16(imp, col0 + 16, w + 16);
+}
+
+// MXFP4 with a window of E8M0 exponents around the OCP one, binary64 argmin
+// (first least in ascending exponent) -- "Bridging the Gap ... Microscaling
+// FP4" page, Method 2: format-specific scale search for E8M0
+template <bool BF16, bool ROT, bool WMSE>
+__global__ __launch_bounds__(kThreads) void mxfp4_sweep(
+    const void* __restrict__ x, int64_t nblocks, int64_t blocks_per_row,
+    const float* __restrict__ imp, int lo, int hi, uint4* __restrict__ codes,
+    uint8_t* __restrict__ scales)
+{
+    for (int64_t blk = (int64_t)blockIdx.x * kThreads + threadIdx.x; blk < nblocks;
+         blk += (int64_t)gridDim.x * kThreads) {
+        float v[32];
+        load_block<32, BF16>(x, blk, v);
+        if constexpr (ROT)
+            fwht<32>(v);
+        const int e0 = mx_exponent(block_absmax<32>(v));
+        float w[32];
+        if constexpr (WMSE)
+            load_weights32(imp, (blk % blocks_per_row) * 32, w);
+        // the first candidate is taken unconditionally, so that a window
+        // whose every error overflows still keeps its first exponent
+        double best = 0.0;
+        int eb = e0, eprev = 1000;
+        for (int k = lo; k <= hi; ++k) {
+            int e = e0 + k;
+            e = e < -127 ? -127 : (e > 127 ? 127 : e);
+            if (e == eprev)
+                continue;
+            const double E = mx_error32<WMSE>(v, w, e);
+            if (eprev == 1000 || E < best) {
+                best = E;
+                eb = e;
+            }
+            eprev = e;
+        }
+        codes[blk] = mx_encode32(v, eb);
+        scales[blk] = (uint8_t)(eb + 127);
+    }
+}
+
+// NVFP4 Four Over Six: the block maximum onto 6 (AbsMax) or onto 4, the
+// lower binary64 error kept, a tie keeps 6 (Adaptive Block-Scaled Data Types
+// page, Problem; ScaleSweep page, Problem definition)
+template <bool BF16, bool ROT, bool WMSE>
+__global__ __launch_bounds__(kThreads) void nvfp4_foursix(
+    const void* __restrict__ x, int64_t nblocks, int64_t blocks_per_row,
+    const float* __restrict__ imp, const float* __restrict__ partials, int npart,
+    float* __restrict__ Sp, uint2* __restrict__ codes, uint8_t* __restrict__ scales)
+{
+    const float S = global_scale(partials, npart, Sp);
+    const float S6 = 6.0f * S, S4 = 4.0f * S;
+    for (int64_t blk = (int64_t)blockIdx.x * kThreads + threadIdx.x; blk < nblocks;
+         blk += (int64_t)gridDim.x * kThreads) {
+        float v[16];
+        load_block<16, BF16>(x, blk, v);
+        if constexpr (ROT)
+            fwht<16>(v);
+        const float a = block_absmax<16>(v);
+        uint32_t cb = 0;
+        float r = 1.0f;
+        if (a != 0.0f) {
+            uint32_t s6 = e4m3_round(a / S6), s4 = e4m3_round(a / S4);
+            s6 = s6 < 1u ? 1u : s6;
+            s4 = s4 < 1u ? 1u : s4;
+            float w[16];
+            if constexpr (WMSE)
+                load_weights16(imp, (blk % blocks_per_row) * 16, w);
+            const float D6 = e4m3_value(s6) * S, r6 = 1.0f / D6;
+            cb = s6;
+            r = r6;
+            if (s4 != s6) {
+                const float D4 = e4m3_value(s4) * S, r4 = 1.0f / D4;
+                if (fp4_error16<WMSE>(v, w, D4, r4) < fp4_error16<WMSE>(v, w, D6, r6)) {
+                    cb = s4;
+                    r = r4;
+                }
+            }
+        }
+        codes[blk] = fp4_encode16(v, r);
+        scales[blk] = (uint8_t)cb;
+    }
+}
+
+// IF4 over a window of patterns: per pattern the FP4 then the INT4 encoding,
+// the first least binary64 error kept
+template <bool BF16, bool ROT, bool WMSE>
+__global__ __launch_bounds__(kThreads) void if4_sweep(
+    const void* __restrict__ x, int64_t nblocks, int64_t blocks_per_row,
+    const float* __restrict__ imp, const float* __restrict__ partials, int npart,
+    float* __restrict__ Sp, int lo, int hi, uint2* __restrict__ codes, uint8_t* __restrict__ scales)
+{
+    __shared__ float4 tab[128]; // D, r, D_int = fl32(D 6/7), r_int
+    const float S = global_scale(partials, npart, Sp);
+    for (int c = threadIdx.x; c < 128; c += kThreads) {
+        const float D = e4m3_value((uint32_t)(c < 0x7E ? c : 0x7E)) * S;
+        const float Di = D * kInt4Step;
+        tab[c] = make_float4(D, 1.0f / D, Di, 1.0f / Di);
+    }
+    __syncthreads();
+    const float S6 = 6.0f * S;
+    for (int64_t blk = (int64_t)blockIdx.x * kThreads + threadIdx.x; blk < nblocks;
+         blk += (int64_t)gridDim.x * kThreads) {
+        float v[16];
+        load_block<16, BF16>(x, blk, v);
+        if constexpr (ROT)
+            fwht<16>(v);
+        const float a = block_absmax<16>(v);
+        uint2 packed;
+        uint32_t sbyte = 0;
+        if (a == 0.0f) {
+            packed = fp4_encode16(v, 1.0f);
+        } else {
+            uint32_t sb = e4m3_round(a / S6);
+            sb = sb < 1u ? 1u : sb;
+            float w[16];
+            if constexpr (WMSE)
+                load_weights16(imp, (blk % blocks_per_row) * 16, w);
+            double best = 0.0;
+            int cb = (int)sb, cprev = -1;
+            for (int k = lo; k <= hi; ++k) {
+                const int c = clamp_pattern((int)sb + k);
+                if (c == cprev)
+                    continue;
+                const float4 t = tab[c];
+                const double Ef = fp4_error16<WMSE>(v, w, t.x, t.y);
+                if (cprev < 0 || Ef < best) { // the first candidate is always taken
+                    best = Ef;
+                    cb = c;
+                }
+                const double Ei = int4_error16<WMSE>(v, w, t.z, t.w);
+                if (Ei < best) {
+                    best = Ei;
+                    cb = c | 0x80;
+                }
+                cprev = c;
+            }
+            const float4 t = tab[cb & 0x7F];
+            packed = (cb & 0x80) ? encode16_int4(v, t.w) : fp4_encode16(v, t.y);
+            sbyte = (uint32_t)cb;
+        }
+        codes[blk] = packed;
+        scales[blk] = (uint8_t)sbyte;
+    }
+}
+
+// FOCUS deploy-side encode: codes from the relaxed step D_q = fl32(D c)
+// (one coefficient per GROUP elements), the stored scale S_dq unchanged
+// (FOCUS page, Method 2: S_q = S_dq c_i; Method 3: c_k per sub-block of 8)
+template <int FMT, bool BF16, int GROUP, bool GIVEN>
+__global__ __launch_bounds__(kThreads) void relaxed_quant(
+    const void* __restrict__ x, int64_t nblocks, const float* __restrict__ coef,
+    const float* __restrict__ partials, int npart, float* __restrict__ Sp,
+    uint8_t* __restrict__ codes, uint8_t* __restrict__ scales)
+{
+    constexpr int B = (FMT == kMXFP4) ? 32 : 16;
+    constexpr int NG = B / GROUP;
+    const float S = (FMT == kMXFP4) ? 1.0f : global_scale(partials, npart, Sp);
+    const float S6 = 6.0f * S;
+    for (int64_t blk = (int64_t)blockIdx.x * kThreads + threadIdx.x; blk < nblocks;
+         blk += (int64_t)gridDim.x * kThreads) {
+        float v[B];
+        load_block<B, BF16>(x, blk, v);
+        uint32_t byte;
+        float D;
+        if constexpr (GIVEN) {
+            // a given byte is a finite non-negative pattern (E8M0 below
+            // 0xFF, E4M3 up to 0x7E)
+            byte = scales[blk];
+            if constexpr (FMT == kMXFP4)
+                D = pow2f((int)byte - 127);
+            else
+                D = e4m3_value(byte) * S;
+        } else if constexpr (FMT == kMXFP4) {
+            const int e = mx_exponent(block_absmax<B>(v));
+            byte = (uint32_t)(e + 127);
+            D = pow2f(e);
+        } else {
+            const float a = block_absmax<B>(v);
+            byte = 0;
+            D = 0.0f;
+            if (a != 0.0f) {
+                byte = e4m3_round(a / S6);
+                byte = byte < 1u ? 1u : byte;
+                D = e4m3_value(byte) * S;
+            }
+        }
+        float c[NG];
+#pragma unroll
+        for (int g = 0; g < NG; ++g)
+            c[g] = coef[blk * NG + g];
+        uint32_t wds[B / 8];
+#pragma unroll
+        for (int q = 0; q < B / 8; ++q) {
+            // one coefficient covers GROUP >= 8 consecutive elements
+            const float cg = c[(8 * q) / GROUP];
+            const float r = (D == 0.0f) ? 0.0f : 1.0f / (D * cg); // a zero step keeps signs only
+            uint32_t wv = 0;
+            wv = fp4_pack2<0>(wv, v[8 * q + 0] * r, v[8 * q + 1] * r);
+            wv = fp4_pack2<1>(wv, v[8 * q + 2] * r, v[8 * q + 3] * r);
+            wv = fp4_pack2<2>(wv, v[8 * q + 4] * r, v[8 * q + 5] * r);
+            wv = fp4_pack2<3>(wv, v[8 * q + 6] * r, v[8 * q + 7] * r);
+            wds[q] = wv;
+        }
+        if constexpr (B == 16)
+            reinterpret_cast<uint2*>(codes)[blk] = make_uint2(wds[0], wds[1]);
+        else
+            reinterpret_cast<uint4*>(codes)[blk] = make_uint4(wds[0], wds[1], wds[2], wds[3]);
+        if constexpr (!GIVEN)
+            scales[blk] = (uint8_t)byte;
+    }
+}
+
 // ---------------------------------------------------------------------------
 // dequantize and error
 // ---------------------------------------------------------------------------
@@ -819,6 +1083,13 @@ static void launch_nvfp4(const QuantArgs& a, int64_t nb, const float* part, int 
     if (a.rule == kAbsMax) {
         hipLaunchKernelGGL((nvfp4_absmax<BF16, ROT>), grid, kThreads, 0, a.stream,
                            a.x, nb, part, npart, Sp, codes, a.scales);
+    } else if (a.rule == kFourSix) {
+        if (a.objective == kWMSE)
+            hipLaunchKernelGGL((nvfp4_foursix<BF16, ROT, true>), grid, kThreads, 0, a.stream,
+                               a.x, nb, bpr, a.importance, part, npart, Sp, codes, a.scales);
+        else
+            hipLaunchKernelGGL((nvfp4_foursix<BF16, ROT, false>), grid, kThreads, 0, a.stream,
+                               a.x, nb, bpr, a.importance, part, npart, Sp, codes, a.scales);
     } else {
         // the pages' two windows get a fully unrolled specialization
         const int win = (a.lo == -3 && a.hi == 7) ? 1 : ((a.lo == -8 && a.hi == 7) ? 2 : 0);
@@ -846,12 +1117,38 @@ static void launch_if4(const QuantArgs& a, int64_t nb, const float* part, int np
     const int64_t bpr = a.cols / 16;
     float* Sp = a.global_scale;
     uint2* codes = reinterpret_cast<uint2*>(a.codes);
-    if (a.objective == kWMSE)
+    const bool wm = a.objective == kWMSE;
+    if (a.rule == kSweep) {
+        if (wm)
+            hipLaunchKernelGGL((if4_sweep<BF16, ROT, true>), grid, kThreads, 0, a.stream, a.x, nb,
+                               bpr, a.importance, part, npart, Sp, a.lo, a.hi, codes, a.scales);
+        else
+            hipLaunchKernelGGL((if4_sweep<BF16, ROT, false>), grid, kThreads, 0, a.stream, a.x, nb,
+                               bpr, a.importance, part, npart, Sp, a.lo, a.hi, codes, a.scales);
+    } else if (wm) {
         hipLaunchKernelGGL((if4_quant<BF16, ROT, true>), grid, kThreads, 0, a.stream,
                            a.x, nb, bpr, a.importance, part, npart, Sp, codes, a.scales);
-    else
+    } else {
         hipLaunchKernelGGL((if4_quant<BF16, ROT, false>), grid, kThreads, 0, a.stream,
                            a.x, nb, bpr, a.importance, part, npart, Sp, codes, a.scales);
+    }
+}
+
+template <bool BF16, bool ROT>
+static void launch_mxfp4(const QuantArgs& a, int64_t nb, int grid)
+{
+    uint4* codes = reinterpret_cast<uint4*>(a.codes);
+    if (a.rule == kSweep) {
+        const int64_t bpr = a.cols / 32;
+        if (a.objective == kWMSE)
+            hipLaunchKernelGGL((mxfp4_sweep<BF16, ROT, true>), grid, kThreads, 0, a.stream, a.x, nb,
+                               bpr, a.importance, a.lo, a.hi, codes, a.scales);
+        else
+            hipLaunchKernelGGL((mxfp4_sweep<BF16, ROT, false>), grid, kThreads, 0, a.stream, a.x, nb,
+                               bpr, a.importance, a.lo, a.hi, codes, a.scales);
+    } else {
+        hipLaunchKernelGGL((mxfp4_quant<BF16, ROT>), grid, kThreads, 0, a.stream, a.x, nb, codes, a.scales);
+    }
 }
 
 template <bool BF16>
@@ -867,26 +1164,37 @@ static void launch_amax(const QuantArgs& a, float* partials, int groups)
     }
 }
 
+// Launches the partial maxima of the global-scale rule when S is computed
+// (NVFP4, IF4) and returns how many there are: 0 means that the quantize
+// kernel reads S from a.global_scale (given by the caller, or written here
+// for an empty tensor).
+static int launch_scale_prologue(const QuantArgs& a)
+{
+    const int64_t n = a.rows * a.cols;
+    float* partials = reinterpret_cast<float*>(a.workspace);
+    if (a.format == kMXFP4 || a.global_scale_given)
+        return 0;
+    if (n == 0) {
+        // nothing to reduce: S = 1 for an empty (all-zero) tensor
+        hipLaunchKernelGGL(finalize_scale, 1, 1024, 0, a.stream, partials, 0, a.global_scale);
+        return 0;
+    }
+    const int64_t items = (a.rotate == 0) ? n * (a.bf16 ? 2 : 4) / 16 : n / 16;
+    const int npart = grid_for(items, kAmaxGroups);
+    if (a.bf16)
+        launch_amax<true>(a, partials, npart);
+    else
+        launch_amax<false>(a, partials, npart);
+    return npart;
+}
+
 hipError_t launch_quantize(const QuantArgs& a)
 {
     const int64_t n = a.rows * a.cols;
     const int B = (a.format == kMXFP4) ? 32 : 16;
     const int64_t nb = n / B;
-    float* partials = reinterpret_cast<float*>(a.workspace);
-    int npart = 0; // 0: the quantize kernel reads S from a.global_scale
-    if (a.format != kMXFP4 && !a.global_scale_given) {
-        if (n > 0) {
-            const int64_t items = (a.rotate == 0) ? n * (a.bf16 ? 2 : 4) / 16 : nb;
-            npart = grid_for(items, kAmaxGroups);
-            if (a.bf16)
-                launch_amax<true>(a, partials, npart);
-            else
-                launch_amax<false>(a, partials, npart);
-        } else {
-            // nothing to reduce: S = 1 for an empty (all-zero) tensor
-            hipLaunchKernelGGL(finalize_scale, 1, 1024, 0, a.stream, partials, 0, a.global_scale);
-        }
-    }
+    const float* partials = reinterpret_cast<const float*>(a.workspace);
+    const int npart = launch_scale_prologue(a);
     if (nb > 0) {
         const int grid = grid_for(nb, kQuantGroupCap);
         const bool rot = a.rotate != 0;
@@ -902,19 +1210,60 @@ hipError_t launch_quantize(const QuantArgs& a)
             else
                 rot ? launch_if4<false, true>(a, nb, part, npart, grid) : launch_if4<false, false>(a, nb, part, npart, grid);
         } else {
-            uint4* codes = reinterpret_cast<uint4*>(a.codes);
-            if (a.bf16) {
-                if (rot)
-                    hipLaunchKernelGGL((mxfp4_quant<true, true>), grid, kThreads, 0, a.stream, a.x, nb, codes, a.scales);
-                else
-                    hipLaunchKernelGGL((mxfp4_quant<true, false>), grid, kThreads, 0, a.stream, a.x, nb, codes, a.scales);
-            } else {
-                if (rot)
-                    hipLaunchKernelGGL((mxfp4_quant<false, true>), grid, kThreads, 0, a.stream, a.x, nb, codes, a.scales);
-                else
-                    hipLaunchKernelGGL((mxfp4_quant<false, false>), grid, kThreads, 0, a.stream, a.x, nb, codes, a.scales);
-            }
+            if (a.bf16)
+                rot ? launch_mxfp4<true, true>(a, nb, grid) : launch_mxfp4<true, false>(a, nb, grid);
+            else
+                rot ? launch_mxfp4<false, true>(a, nb, grid) : launch_mxfp4<false, false>(a, nb, grid);
         }
+    }
+    return hipGetLastError();
+}
+
+template <int FMT, bool BF16, int GROUP>
+static void launch_relaxed_g(const RelaxArgs& a, int64_t nb, const float* part, int npart, int grid)
+{
+    if (a.scales_given)
+        hipLaunchKernelGGL((relaxed_quant<FMT, BF16, GROUP, true>), grid, kThreads, 0, a.stream,
+                           a.x, nb, a.coef, part, npart, a.global_scale, a.codes, a.scales);
+    else
+        hipLaunchKernelGGL((relaxed_quant<FMT, BF16, GROUP, false>), grid, kThreads, 0, a.stream,
+                           a.x, nb, a.coef, part, npart, a.global_scale, a.codes, a.scales);
+}
+
+template <int FMT, bool BF16>
+static void launch_relaxed_f(const RelaxArgs& a, int64_t nb, const float* part, int npart, int grid)
+{
+    constexpr int B = (FMT == kMXFP4) ? 32 : 16;
+    if (a.group == 8)
+        launch_relaxed_g<FMT, BF16, 8>(a, nb, part, npart, grid);
+    else
+        launch_relaxed_g<FMT, BF16, B>(a, nb, part, npart, grid);
+}
+
+hipError_t launch_quantize_relaxed(const RelaxArgs& r)
+{
+    QuantArgs a{};
+    a.format = r.format;
+    a.global_scale_given = r.global_scale_given;
+    a.bf16 = r.bf16;
+    a.x = r.x;
+    a.rows = r.rows;
+    a.cols = r.cols;
+    a.global_scale = r.global_scale;
+    a.workspace = r.workspace;
+    a.stream = r.stream;
+    const int npart = launch_scale_prologue(a);
+    const int B = (r.format == kMXFP4) ? 32 : 16;
+    const int64_t nb = r.rows * r.cols / B;
+    if (nb > 0) {
+        const int grid = grid_for(nb, kQuantGroupCap);
+        const float* part = reinterpret_cast<const float*>(r.workspace);
+        if (r.format == kMXFP4)
+            r.bf16 ? launch_relaxed_f<kMXFP4, true>(r, nb, part, npart, grid)
+                   : launch_relaxed_f<kMXFP4, false>(r, nb, part, npart, grid);
+        else
+            r.bf16 ? launch_relaxed_f<kNVFP4, true>(r, nb, part, npart, grid)
+                   : launch_relaxed_f<kNVFP4, false>(r, nb, part, npart, grid);
     }
     return hipGetLastError();
 }

@@ -8,7 +8,7 @@
 namespace fp4q {
 
 enum { kNVFP4 = 0, kMXFP4 = 1, kIF4 = 2 };
-enum { kAbsMax = 0, kSweep = 1 };
+enum { kAbsMax = 0, kSweep = 1, kFourSix = 2 };
 enum { kMSE = 0, kWMSE = 1 };
 
 // workspace layout (bytes): [0, 16384) partial maxima (float, <= 1024) or
@@ -54,7 +54,22 @@ struct ErrorArgs {
     hipStream_t stream;
 };
 
+// codes from a relaxed step D*c, stored scales unchanged
+struct RelaxArgs {
+    int format, group;
+    bool global_scale_given, scales_given, bf16;
+    const void* x;
+    int64_t rows, cols;
+    const float* coef;
+    uint8_t* codes;
+    uint8_t* scales;
+    float* global_scale;
+    void* workspace;
+    hipStream_t stream;
+};
+
 hipError_t launch_quantize(const QuantArgs& a);
+hipError_t launch_quantize_relaxed(const RelaxArgs& a);
 hipError_t launch_dequantize(const DequantArgs& a);
 hipError_t launch_error(const ErrorArgs& a, double* out_dev);
 

@@ -52,21 +52,25 @@
 extern "C" {
 #endif
 
-#define FP4Q_ABI_VERSION 1
+#define FP4Q_ABI_VERSION 2
 
 typedef enum {
     FP4Q_OK = 0,
     FP4Q_E_NULL = -1,        /* a required pointer is NULL                   */
     FP4Q_E_ARG = -2,         /* bad enum, window, rotation or workspace size */
     FP4Q_E_SHAPE = -3,       /* negative sizes or cols % block != 0          */
-    FP4Q_E_UNSUPPORTED = -4, /* a valid combination this library lacks       */
+    FP4Q_E_UNSUPPORTED = -4, /* a combination outside the methods' scope     */
     FP4Q_E_HIP = -5,         /* the HIP runtime refused a launch or copy     */
     FP4Q_E_ALIGN = -6        /* a tensor pointer is not aligned as required  */
 } fp4q_status;
 
 typedef enum { FP4Q_NVFP4 = 0, FP4Q_MXFP4 = 1, FP4Q_IF4 = 2 } fp4q_format;
 typedef enum { FP4Q_F32 = 0, FP4Q_BF16 = 1 } fp4q_dtype;
-typedef enum { FP4Q_SCALE_ABSMAX = 0, FP4Q_SCALE_SWEEP = 1 } fp4q_scale_rule;
+typedef enum {
+    FP4Q_SCALE_ABSMAX = 0,
+    FP4Q_SCALE_SWEEP = 1,
+    FP4Q_SCALE_FOUR_OVER_SIX = 2
+} fp4q_scale_rule;
 typedef enum { FP4Q_OBJ_MSE = 0, FP4Q_OBJ_WMSE = 1 } fp4q_objective;
 
 /* The problem statement of one quantization.
@@ -74,17 +78,32 @@ typedef enum { FP4Q_OBJ_MSE = 0, FP4Q_OBJ_WMSE = 1 } fp4q_objective;
  *   block       16 for NVFP4 and IF4, 32 for MXFP4.
  *   scale_rule  ABSMAX: the block scale is the block maximum mapped onto the
  *               FP4 maximum 6 and rounded to FP8 ("AbsMax", ScaleSweep page,
- *               Problem definition).  SWEEP: ScaleSweep -- every E4M3 bit
- *               pattern s_base + k, k in [sweep_lo, sweep_hi], is tried and
- *               the one of least block error kept (ScaleSweep page, Method 2
- *               and 3).  SWEEP is NVFP4-only.
+ *               Problem definition).
+ *               SWEEP: a window of scales around the AbsMax one is tried and
+ *               the one of least block error kept.
+ *                 NVFP4: ScaleSweep -- every E4M3 bit pattern s_base + k,
+ *                 k in [sweep_lo, sweep_hi] (ScaleSweep page, Method 2 and 3).
+ *                 MXFP4: every E8M0 exponent e_base + k ("Bridging the Gap
+ *                 ... Microscaling FP4" page, Method 2, format-specific
+ *                 scale search).
+ *                 IF4: every pattern s_base + k, each with FP4 then with INT4
+ *                 codes (the IF4 pick of the Adaptive Block-Scaled Data Types
+ *                 page, Methodology, run at every pattern of the window).
+ *               FOUR_OVER_SIX (NVFP4 only): the block maximum is mapped onto
+ *               6 or onto 4, E4M3(a / (6 S)) vs E4M3(a / (4 S)), and the one
+ *               of lower block error kept, 6 on a tie (Adaptive Block-Scaled
+ *               Data Types page, Problem; ScaleSweep page, Problem definition).
+ *               Every choice compares binary64 block errors of the binary32
+ *               encodes; an exact tie keeps the candidate tried first.
  *   objective   MSE, or WMSE weighted by a per-column importance vector
- *               (ScaleSweep page, Method 1).  Used by SWEEP and by IF4's
- *               FP4-vs-INT4 pick.
+ *               (ScaleSweep page, Method 1).  Used wherever block errors
+ *               decide: SWEEP, FOUR_OVER_SIX and IF4's FP4-vs-INT4 pick.
  *   sweep_lo, sweep_hi
- *               the window of bit-pattern offsets, -126 <= lo <= hi <= 126;
- *               the pages use [-3, 7] for MSE and [-8, 7] for WMSE.
- *               Patterns outside [0x01, 0x7E] are skipped.
+ *               the window of offsets, -126 <= lo <= hi <= 126; the pages use
+ *               [-3, 7] for MSE and [-8, 7] for WMSE (NVFP4).  An offset that
+ *               leads past the ends of the scale range (E4M3 patterns 0x01 and
+ *               0x7E, E8M0 exponents -127 and 127) stands for that end, and
+ *               each scale is tried once.
  *   rotate      0, or equal to block: apply the orthonormal Sylvester block
  *               Hadamard transform to every block before quantizing
  *               ("Bridging the Gap ... Microscaling FP4" page, Method 1).
@@ -123,11 +142,37 @@ size_t fp4q_workspace_bytes(const fp4q_spec* spec, int64_t rows, int64_t cols);
  * |x| * fl32(1 / fl32(s S)) (ties to the even code, saturating at 6).  IF4
  * also encodes the block as integers q = round(|x| / (D 6/7)) clamped to 7
  * and keeps INT4 only when its error is strictly lower.  MXFP4 uses the
- * power of two 2^(floor(log2 a) - 2). */
+ * power of two 2^(floor(log2 a) - 2).  SWEEP and FOUR_OVER_SIX then choose
+ * among the scales listed at fp4q_spec. */
 fp4q_status fp4q_quantize(const fp4q_spec* spec, const void* x, int32_t x_dtype,
                           int64_t rows, int64_t cols, const float* importance,
                           uint8_t* codes, uint8_t* scales, float* global_scale,
                           void* workspace, size_t ws_bytes, void* stream);
+
+/* Deploy-side encode of FOCUS (FOCUS page, Method 2, coupled-relaxation
+ * scaling: the quantization scale S_q = S_dq c while the stored
+ * dequantization scale stays S_dq; Method 3, dual-granularity scaling: one
+ * coefficient c per sub-block of 8 under a shared S_dq).  spec->format is
+ * NVFP4 or MXFP4, spec->rotate 0; scale_rule, objective and the window are
+ * ignored; global_scale_given as for fp4q_quantize.
+ *   coef        fp32 [rows, cols / coef_group], positive and finite, the
+ *               learned relaxation coefficients; row-major, so block b of a
+ *               row owns coef[row][b*block/coef_group ...].
+ *   coef_group  8 (dual granularity) or spec->block (one per block).
+ *   scales_given 0: S_dq is the AbsMax scale (as fp4q_quantize with
+ *               FP4Q_SCALE_ABSMAX) and is written to scales; 1: scales is an
+ *               input of finite non-negative bytes (E4M3 0x00..0x7E, E8M0
+ *               0x00..0xFE) and is not written.
+ * Per element, with D the step of S_dq (fl32(s S), or 2^(byte-127)):
+ * D_q = fl32(D c), code = E2M1 nearest to fl32(|x| fl32(1 / D_q)), ties to
+ * the even code, saturating at 6; a block with D = 0 gets sign-only codes.
+ * fp4q_dequantize of the result applies S_dq, as the method intends.
+ * Alignment: x 16, codes 8 (16 for MXFP4), coef 4, workspace 256 bytes. */
+fp4q_status fp4q_quantize_relaxed(const fp4q_spec* spec, const void* x, int32_t x_dtype,
+                                  int64_t rows, int64_t cols, const float* coef,
+                                  int32_t coef_group, int32_t scales_given,
+                                  uint8_t* codes, uint8_t* scales, float* global_scale,
+                                  void* workspace, size_t ws_bytes, void* stream);
 
 /* Dequantize codes/scales/S into y [rows, cols] (y_dtype FP4Q_F32 or
  * FP4Q_BF16, 16-byte aligned): x_hat = +-value(code) * D, D = fl32(s S) for

@@ -38,7 +38,7 @@ def test_library_exports_every_declared_symbol(L):
 
 
 def test_abi_version_and_status_strings(L):
-    assert L.fp4q_abi_version() == 1
+    assert L.fp4q_abi_version() == 2
     for st in B.STATUS:
         assert L.fp4q_status_string(st)
     assert L.fp4q_status_string(-99) == b"unknown status"
@@ -75,7 +75,10 @@ def test_workspace_bytes(L):
     (dict(scale_rule=B.FP4Q_SCALE_SWEEP, sweep_lo=3, sweep_hi=2), -2),
     (dict(scale_rule=B.FP4Q_SCALE_SWEEP, sweep_lo=-127), -2),
     (dict(scale_rule=B.FP4Q_SCALE_SWEEP, sweep_hi=127), -2),
-    (dict(scale_rule=B.FP4Q_SCALE_SWEEP, format=B.FP4Q_IF4), -4),
+    (dict(scale_rule=B.FP4Q_SCALE_FOUR_OVER_SIX, format=B.FP4Q_IF4), -4),  # 4/6 is NVFP4-only
+    (dict(scale_rule=B.FP4Q_SCALE_FOUR_OVER_SIX, format=B.FP4Q_MXFP4, block=32), -4),
+    (dict(scale_rule=B.FP4Q_SCALE_SWEEP, format=B.FP4Q_MXFP4, block=32, sweep_lo=2, sweep_hi=1), -2),
+    (dict(scale_rule=B.FP4Q_SCALE_SWEEP, format=B.FP4Q_IF4, sweep_hi=127), -2),
 ])
 def test_quantize_rejects_bad_spec(L, kw, status):
     assert q(L, spec(**kw)) == status
@@ -98,6 +101,42 @@ def test_quantize_rejects_bad_arguments(L):
     assert q(L, spec(), codes=C.c_void_p(0x10004)) == -6
     assert q(L, spec(), ws=C.c_void_p(0x10080)) == -6
     assert q(L, w, imp=C.c_void_p(0x10004)) == -6
+    # every rule whose choice compares block errors needs the weights
+    for kw in (dict(scale_rule=B.FP4Q_SCALE_FOUR_OVER_SIX),
+               dict(format=B.FP4Q_MXFP4, block=32, scale_rule=B.FP4Q_SCALE_SWEEP),
+               dict(format=B.FP4Q_IF4, scale_rule=B.FP4Q_SCALE_SWEEP),
+               dict(format=B.FP4Q_IF4)):
+        assert q(L, spec(objective=B.FP4Q_OBJ_WMSE, **kw), imp=None) == -1, kw
+
+
+COEF = C.c_void_p(0x70000)
+
+
+def rq(L, s, x=X, dtype=B.FP4Q_BF16, rows=4, cols=64, coef=COEF, group=16, given=0,
+       codes=CODES, scales=SCALES, gs=GS, ws=WS, ws_bytes=1 << 20):
+    return L.fp4q_quantize_relaxed(C.byref(s) if s is not None else None, x, dtype, rows, cols,
+                                   coef, group, given, codes, scales, gs, ws, ws_bytes, None)
+
+
+def test_quantize_relaxed_rejects_bad_arguments(L):
+    mx = spec(format=B.FP4Q_MXFP4, block=32)
+    assert rq(L, None) == -1
+    assert rq(L, spec(), coef=None) == -1
+    assert rq(L, spec(), x=None) == -1
+    assert rq(L, spec(), scales=None) == -1
+    assert rq(L, spec(), gs=None) == -1                                  # NVFP4 needs S
+    assert rq(L, spec(), ws=None) == -1
+    assert rq(L, spec(format=B.FP4Q_IF4)) == -4                          # relaxed FP4 only
+    assert rq(L, spec(rotate=16)) == -4
+    assert rq(L, spec(), group=4) == -2
+    assert rq(L, spec(), group=32) == -2                                 # 8 or the block
+    assert rq(L, mx, group=16) == -2
+    assert rq(L, spec(), given=2) == -2
+    assert rq(L, spec(), dtype=3) == -2
+    assert rq(L, spec(), cols=40) == -3
+    assert rq(L, spec(), ws_bytes=64) == -2
+    assert rq(L, spec(), coef=C.c_void_p(0x70002)) == -6
+    assert rq(L, mx, group=8, codes=C.c_void_p(0x10008)) == -6          # MXFP4 codes 16-aligned
 
 
 def test_dequantize_and_error_reject_bad_arguments(L):

@@ -168,3 +168,72 @@ def test_c5_kv_sweep_hadamard(B, ref):
     e = ref.error(x, gc, gsc, S, rotate=16, nthreads=THREADS)[0]
     assert abs(mse - e) <= 1e-9 * e
     print(f"c5: MSE {mse:.6g}")
+
+
+# ---------------------------------------------------------------------------
+# the extension rules at full size
+# ---------------------------------------------------------------------------
+
+def test_c2_four_over_six_wmse(B, ref, c2data):
+    x, imp = c2data
+    xd, impd = to_dev(x), to_dev(imp)
+    codes, scales, gs = B.quantize(xd, scale_rule=B.FP4Q_SCALE_FOUR_OVER_SIX, objective=1,
+                                   importance=impd)
+    full = ref.quantize(x, rule=ref.FOUR_SIX, objective=ref.WMSE, importance=imp,
+                        nthreads=THREADS)
+    assert gs.item() == np.float32(full["S"])
+    assert np.array_equal(full["scales"], scales.cpu().numpy())
+    assert np.array_equal(full["codes"], codes.cpu().numpy())
+    wm = B.error(xd, codes, scales, gs, importance=impd)[1]
+    base = B.quantize(xd)
+    wb = B.error(xd, *base, importance=impd)[1]
+    print(f"c2 4/6: WMSE {wm:.6g} vs AbsMax {wb:.6g}")
+    assert wm < wb
+
+
+@pytest.mark.parametrize("rotate", [0, 32])
+def test_c3_mxfp4_exponent_window(B, ref, rotate):
+    x = synth.c3()
+    xd = to_dev(x)
+    codes, scales, _ = B.quantize(xd, format=B.FP4Q_MXFP4, scale_rule=B.FP4Q_SCALE_SWEEP,
+                                  rotate=rotate)
+    want = ref.quantize(x, fmt=ref.MXFP4, rule=ref.SWEEP, window=(0, 1), rotate=rotate,
+                        nthreads=THREADS)
+    assert np.array_equal(scales.cpu().numpy(), want["scales"])
+    assert np.array_equal(codes.cpu().numpy(), want["codes"])
+    mse = B.error(xd, codes, scales, None, format=B.FP4Q_MXFP4, rotate=rotate)[0]
+    base = B.quantize(xd, format=B.FP4Q_MXFP4, rotate=rotate)
+    mb = B.error(xd, *base, format=B.FP4Q_MXFP4, rotate=rotate)[0]
+    print(f"c3 rotate={rotate} window [0,1]: MSE {mse:.6g} vs OCP {mb:.6g}")
+    assert mse <= mb
+
+
+def test_c4_if4_sweep(B, ref):
+    x, _ = synth.c4()
+    xd = to_dev(x)
+    codes, scales, gs = B.quantize(xd, format=B.FP4Q_IF4, scale_rule=B.FP4Q_SCALE_SWEEP,
+                                   window=(-3, 7))
+    want = ref.quantize(x, fmt=ref.IF4, rule=ref.SWEEP, window=(-3, 7), nthreads=THREADS)
+    assert gs.item() == np.float32(want["S"])
+    assert np.array_equal(scales.cpu().numpy(), want["scales"])
+    assert np.array_equal(codes.cpu().numpy(), want["codes"])
+    mse = B.error(xd, codes, scales, gs, format=B.FP4Q_IF4)[0]
+    base = B.quantize(xd, format=B.FP4Q_IF4)
+    mb = B.error(xd, *base, format=B.FP4Q_IF4)[0]
+    print(f"c4 IF4 + sweep [-3,7]: MSE {mse:.6g} vs IF4 {mb:.6g}")
+    assert mse <= mb
+
+
+@pytest.mark.parametrize("fmt,group", [("nvfp4", 8), ("mxfp4", 8)])
+def test_relaxed_full(B, ref, c2data, fmt, group):
+    x = c2data[0] if fmt == "nvfp4" else synth.c3()
+    f = B.FP4Q_MXFP4 if fmt == "mxfp4" else B.FP4Q_NVFP4
+    rows, cols = x.shape
+    c = np.random.default_rng(12).lognormal(0.0, 0.08, (rows, cols // group)).astype(np.float32)
+    codes, scales, gs = B.quantize_relaxed(to_dev(x), to_dev(c), group, format=f)
+    want = ref.quantize_relaxed(x, c, group, fmt=ref.MXFP4 if fmt == "mxfp4" else ref.NVFP4,
+                                nthreads=THREADS)
+    if fmt == "nvfp4":
+        assert gs.item() == np.float32(want["S"])
+    assert np.array_equal(scales.cpu().numpy(), want["scales"])
+    assert np.array_equal(codes.cpu().numpy(), want["codes"])
