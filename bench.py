@@ -13,7 +13,9 @@ call; `roofline` is the dominant kernel (the sweep quantizer) timed alone
 with HIP events on the stream it runs on, against the 8 TB/s HBM peak;
 `cpu_baseline` is the CPU oracle on a bounded row sample of the same
 workload, and `parity_sample` compares the GPU's bytes on those rows with the
-oracle's.  `secondary` holds the 2 GiB KV-cache workload (NVFP4 ScaleSweep MSE
+oracle's.  `extensions` times Four Over Six, the MXFP4 exponent window, the
+IF4 pattern window and the FOCUS deploy encode.  `secondary` holds the 2 GiB
+KV-cache workload (NVFP4 ScaleSweep MSE
 [-3, 7] with a fused 16-point Hadamard; quantize and dequantize timed
 separately).  A plain 1 GiB device copy is the achievable-bandwidth yardstick.
 """
@@ -101,6 +103,82 @@ def event_time(fn, steps, warmup):
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     return s.elapsed_time(e) / steps, wall
+
+
+def extensions(args, B, synth, dev, x2, imp, ws):
+    """The rules beyond ScaleSweep, each timed as one quantize call (global
+    scale computed) on its workload, with its MSE next to its baseline rule."""
+    import torch
+    steps = max(5, args.steps // 5)
+    out = {}
+
+    def run(name, workload, x, spec, importance=None, base_spec=None, err_imp=None, rotate=0,
+            bytes_per_elem=None):
+        rows, cols = x.shape
+        n = rows * cols
+        codes = torch.empty(n // 2, dtype=torch.uint8, device=dev)
+        scales = torch.empty(n // spec.block, dtype=torch.uint8, device=dev)
+        gs = torch.empty(1, dtype=torch.float32, device=dev)
+        # enough copies (>= 512 MiB) that no step finds its input in the Infinity Cache
+        ncopy = max(2, -(-(512 << 20) // (x.numel() * x.element_size())))
+        xc = [x] + [x.clone() for _ in range(ncopy - 1)]
+        ms, _ = event_time(lambda i: B.fp4q_quantize(spec, xc[i % ncopy], importance, codes, scales,
+                                                     gs, ws), steps, 2)
+        del xc
+        espec = B.make_spec(spec.format, rotate=rotate)
+        e = B.fp4q_error(espec, x, err_imp, codes, scales, gs, ws)
+        B.fp4q_quantize(base_spec, x, importance, codes, scales, gs, ws)
+        eb = B.fp4q_error(espec, x, err_imp, codes, scales, gs, ws)
+        k = 1 if err_imp is not None else 0
+        gbps = n * bytes_per_elem / (ms * 1e-3) / 1e9
+        out[name] = {"workload": workload, "quantize_ms": ms,
+                     "quantize_gelem_s": n / (ms * 1e-3) / 1e9, "quantize_gbps": gbps,
+                     "quantize_frac_of_peak": gbps / PEAK_HBM_GBPS,
+                     "error": e[k], "baseline_error": eb[k],
+                     "error_kind": "wmse" if k else "mse"}
+        log(f"{name}: {ms:.3f} ms, {gbps:.0f} GB/s, err {e[k]:.6g} vs baseline {eb[k]:.6g}")
+        del codes, scales
+
+    nv = 2 * 2.0 + 0.5 + 1.0 / 16          # global max read + read + codes + scales
+    mx = 2.0 + 0.5 + 1.0 / 32
+    run("nvfp4_four_over_six_wmse_c2",
+        "NVFP4 Four Over Six (max onto 6 or 4), WMSE, bf16 weight 14336x4096; baseline AbsMax",
+        x2, B.make_spec(B.FP4Q_NVFP4, B.FP4Q_SCALE_FOUR_OVER_SIX, B.FP4Q_OBJ_WMSE),
+        importance=imp, base_spec=B.make_spec(), err_imp=imp, bytes_per_elem=nv)
+
+    x3 = to_dev(synth.c3(), dev)
+    for rot in (0, 32):
+        run(f"mxfp4_exponent_window_rot{rot}_c3",
+            f"MXFP4 E8M0 exponent window [0,1], MSE, rotation {rot}, bf16 activations "
+            "8192x4096 with 8 outlier channels; baseline the OCP exponent",
+            x3, B.make_spec(B.FP4Q_MXFP4, B.FP4Q_SCALE_SWEEP, window=(0, 1), rotate=rot),
+            base_spec=B.make_spec(B.FP4Q_MXFP4, rotate=rot), rotate=rot, bytes_per_elem=mx)
+    c = torch.from_numpy(np.random.default_rng(12).lognormal(0.0, 0.08, (8192, 4096 // 8))
+                         .astype(np.float32)).to(dev)
+    r3 = torch.empty(8192 * 4096 // 2, dtype=torch.uint8, device=dev)
+    s3 = torch.empty(8192 * 4096 // 32, dtype=torch.uint8, device=dev)
+    spec_r = B.make_spec(B.FP4Q_MXFP4)
+    x3c = [x3] + [x3.clone() for _ in range(7)]
+    ms, _ = event_time(lambda i: B.fp4q_quantize_relaxed(spec_r, x3c[i % 8], c, 8, False, r3, s3,
+                                                         None, ws), steps, 2)
+    del x3c
+    gb = 8192 * 4096 * (mx + 4.0 / 8) / (ms * 1e-3) / 1e9
+    out["mxfp4_focus_deploy_g8_c3"] = {
+        "workload": "FOCUS deploy encode, MXFP4, one coefficient per 8 elements "
+                    "(lognormal(0,0.08)), bf16 8192x4096", "quantize_ms": ms,
+        "quantize_gbps": gb, "quantize_frac_of_peak": gb / PEAK_HBM_GBPS}
+    log(f"mxfp4 focus g8: {ms:.3f} ms, {gb:.0f} GB/s")
+    del x3, c, r3, s3
+
+    x4 = to_dev(synth.c4()[0], dev)
+    run("if4_pattern_window_c4",
+        "IF4 (FP4 or INT4 per block) over E4M3 patterns [-3,7], MSE, bf16 8192x8192 "
+        "half uniform / half spiky-Laplace blocks; baseline plain IF4",
+        x4, B.make_spec(B.FP4Q_IF4, B.FP4Q_SCALE_SWEEP, window=(-3, 7)),
+        base_spec=B.make_spec(B.FP4Q_IF4), bytes_per_elem=nv)
+    del x4
+    torch.cuda.empty_cache()
+    return out
 
 
 def main():
@@ -247,6 +325,10 @@ def main():
             "oracle_near_tie_blocks": int(np.sum(gap < 1e-6)),
         }
         log(f"parity on the sample: {result['parity_sample']}")
+
+    # ---------------- extensions: 4/6, MXFP4 exponent window, IF4 window, FOCUS ----------------
+    if not args.no_secondary:
+        result["extensions"] = extensions(args, B, synth, dev, xs[0], imp, ws)
 
     # ---------------- secondary: KV cache, sweep MSE + fused Hadamard ----------------
     if not args.no_secondary:
