@@ -263,8 +263,10 @@ __global__ __launch_bounds__(kThreads) void nvfp4_absmax(
 // when PAIR, also for y_i / 2 (the pattern eight steps up, whose step is
 // exactly 2D) in units of the first step: the hardware conversion applies the
 // power-of-two scale 2 exactly, so one multiply serves both candidates.
+// With weights, b holds sqrt(w) and each term is formed as (b y - b q)^2, so
+// that the product b y serves both candidates of a pair as well.
 template <bool WMSE, bool PAIR>
-__device__ __forceinline__ void fp4_err32(const float* v, const float* w, float r, float& F1, float& F2)
+__device__ __forceinline__ void fp4_err32(const float* v, const float* b, float r, float& F1, float& F2)
 {
     F1 = 0.0f;
     F2 = 0.0f;
@@ -295,11 +297,22 @@ __device__ __forceinline__ void fp4_err32(const float* v, const float* w, float 
         }
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-            const float d = y[j] - q[j];
-            F1 = __builtin_fmaf(WMSE ? d * w[8 * g + j] : d, d, F1);
-            if constexpr (PAIR) {
-                const float e = y[j] - h[j];
-                F2 = __builtin_fmaf(WMSE ? e * w[8 * g + j] : e, e, F2);
+            if constexpr (WMSE) {
+                const float bj = b[8 * g + j];
+                const float by = bj * y[j];
+                const float d = __builtin_fmaf(-bj, q[j], by);
+                F1 = __builtin_fmaf(d, d, F1);
+                if constexpr (PAIR) {
+                    const float e = __builtin_fmaf(-bj, h[j], by);
+                    F2 = __builtin_fmaf(e, e, F2);
+                }
+            } else {
+                const float d = y[j] - q[j];
+                F1 = __builtin_fmaf(d, d, F1);
+                if constexpr (PAIR) {
+                    const float e = y[j] - h[j];
+                    F2 = __builtin_fmaf(e, e, F2);
+                }
             }
         }
     }
@@ -323,7 +336,7 @@ __device__ __forceinline__ void keep_best(float E, int c, float& e1, float& e2, 
 // clamps or masks (evaluation order differs from ascending k, which only
 // matters for exact ties, and those are never certified)
 template <bool WMSE, int LO, int HI>
-__device__ __forceinline__ void sweep_fixed(const float* v, const float* w, const float4* tab, int sb,
+__device__ __forceinline__ void sweep_fixed(const float* v, const float* b, const float4* tab, int sb,
                                             float& e1, float& e2, int& cb)
 {
 #pragma unroll
@@ -334,17 +347,18 @@ __device__ __forceinline__ void sweep_fixed(const float* v, const float* w, cons
         const float4 t = tab[c];
         float F1, F2;
         if (k + 8 <= HI) {
-            fp4_err32<WMSE, true>(v, w, t.y, F1, F2);
+            fp4_err32<WMSE, true>(v, b, t.y, F1, F2);
             keep_best(F1 * t.z, c, e1, e2, cb);
             keep_best(F2 * t.z, c + 8, e1, e2, cb);
         } else {
-            fp4_err32<WMSE, false>(v, w, t.y, F1, F2);
+            fp4_err32<WMSE, false>(v, b, t.y, F1, F2);
             keep_best(F1 * t.z, c, e1, e2, cb);
         }
     }
 }
 
 constexpr int kQueueCap = 1024; // fallback queue entries per workgroup (LDS)
+constexpr int kRootCols = 4096; // importance columns whose square roots fit in LDS
 
 template <bool BF16, bool ROT, bool WMSE, int WIN>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) void nvfp4_sweep(
@@ -352,18 +366,38 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
     const float* __restrict__ imp, const float* __restrict__ partials, int npart,
     float* __restrict__ Sp, int lo, int hi, uint2* __restrict__ codes, uint8_t* __restrict__ scales)
 {
-    // per pattern: D = fl32(s S), r = fl32(1/D), fl32(D*D), and 1 when the
+    // per pattern: D = fl32(s S), r = fl32(1/D), s*s (exact), and 1 when the
     // pattern eight steps up has exactly twice this step (so one product
-    // serves both), else 0
+    // serves both), else 0.  Estimates are kept in units of S^2: s*s is
+    // normal for every pattern, while D*D would underflow for small S.
     __shared__ float4 tab[128];
     __shared__ int64_t queue[kQueueCap];
     __shared__ uint32_t qn;
+    // sqrt(importance) per column and the importance sum per block column
+    __shared__ float root[WMSE ? kRootCols : 1];
+    __shared__ float wsum[WMSE ? kRootCols / 16 : 1];
     const float S = global_scale(partials, npart, Sp);
     for (int c = threadIdx.x; c < 128; c += kThreads) {
-        const float D = e4m3_value((uint32_t)(c < 0x7E ? c : 0x7E)) * S;
+        const float sc = e4m3_value((uint32_t)(c < 0x7E ? c : 0x7E));
+        const float D = sc * S;
         const float D8 = e4m3_value((uint32_t)(c + 8 < 0x7E ? c + 8 : 0x7E)) * S;
         const bool twice = c >= 8 && c + 8 <= 0x7E && D8 == 2.0f * D && (1.0f / D8) == 0.5f * (1.0f / D);
-        tab[c] = make_float4(D, 1.0f / D, D * D, twice ? 1.0f : 0.0f);
+        tab[c] = make_float4(D, 1.0f / D, sc * sc, twice ? 1.0f : 0.0f);
+    }
+    const int64_t cols = blocks_per_row * 16;
+    const bool roots_in_lds = WMSE && cols <= kRootCols;
+    if constexpr (WMSE) {
+        if (roots_in_lds) {
+            for (int j = threadIdx.x; j < (int)cols; j += kThreads)
+                root[j] = __builtin_sqrtf(imp[j]);
+            for (int j = threadIdx.x; j < (int)blocks_per_row; j += kThreads) {
+                float W = 0.0f;
+#pragma unroll
+                for (int i = 0; i < 16; ++i)
+                    W += imp[16 * j + i];
+                wsum[j] = W;
+            }
+        }
     }
     if (threadIdx.x == 0)
         qn = 0;
@@ -373,6 +407,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
     const bool pairs_exact = __syncthreads_and(threadIdx.x < 8 || threadIdx.x > 0x76 || tab[threadIdx.x].w != 0.0f);
     constexpr int FLO = WIN == 1 ? -3 : -8, FHI = 7;
     const float S6 = 6.0f * S;
+    const float invS = 1.0f / S;
     constexpr float u = 0x1p-24f; // unit roundoff of binary32
     const int64_t stride = (int64_t)gridDim.x * kThreads;
     // importance column of this lane's block, advanced incrementally
@@ -453,20 +488,32 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
                 sb = sb < 1u ? 1u : sb;
                 // this lane's offsets that land on finite patterns
                 const int klo = max(lo, 1 - (int)sb), khi = min(hi, 0x7E - (int)sb);
-                float w[16];
+                float b[16];
                 float W = 16.0f;
                 if constexpr (WMSE) {
-                    load_weights16(imp, col * 16, w);
-                    W = 0.0f;
+                    if (roots_in_lds) {
+                        const float4* rp = reinterpret_cast<const float4*>(root + col * 16);
 #pragma unroll
-                    for (int i = 0; i < 16; ++i)
-                        W += w[i];
+                        for (int q = 0; q < 4; ++q) {
+                            const float4 t = rp[q];
+                            b[4 * q + 0] = t.x; b[4 * q + 1] = t.y; b[4 * q + 2] = t.z; b[4 * q + 3] = t.w;
+                        }
+                        W = wsum[col];
+                    } else {
+                        load_weights16(imp, col * 16, b);
+                        W = 0.0f;
+#pragma unroll
+                        for (int i = 0; i < 16; ++i) {
+                            W += b[i];
+                            b[i] = __builtin_sqrtf(b[i]);
+                        }
+                    }
                 }
                 float e1 = __builtin_huge_valf(), e2 = __builtin_huge_valf();
                 int cb = 1;
                 const bool interior = WIN != 0 && pairs_exact && (int)sb + FLO >= 8 && (int)sb + FHI <= 0x7E;
                 if (WIN != 0 && __builtin_amdgcn_ballot_w64(!interior) == 0) {
-                    sweep_fixed<WMSE, FLO, FHI>(v, w, tab, (int)sb, e1, e2, cb);
+                    sweep_fixed<WMSE, FLO, FHI>(v, b, tab, (int)sb, e1, e2, cb);
                 } else
                 // offsets k and k+8 pair up in runs of eight; the rest are singles
                 for (int k = lo; k <= hi; ++k) {
@@ -481,26 +528,33 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
                         float F1, F2, E2;
                         if (__builtin_amdgcn_ballot_w64(t.w == 0.0f) == 0) {
                             // every lane's pair is an exact doubling: shared product
-                            fp4_err32<WMSE, true>(v, w, t.y, F1, F2);
+                            fp4_err32<WMSE, true>(v, b, t.y, F1, F2);
                             E2 = F2 * t.z;
                         } else {
                             float unused;
-                            fp4_err32<WMSE, false>(v, w, t.y, F1, unused);
-                            fp4_err32<WMSE, false>(v, w, tab[c8].y, F2, unused);
+                            fp4_err32<WMSE, false>(v, b, t.y, F1, unused);
+                            fp4_err32<WMSE, false>(v, b, tab[c8].y, F2, unused);
                             E2 = F2 * tab[c8].z;
                         }
                         keep_best(ok1 ? F1 * t.z : __builtin_huge_valf(), c, e1, e2, cb);
                         keep_best(ok2 ? E2 : __builtin_huge_valf(), c8, e1, e2, cb);
                     } else {
                         float F1, unused;
-                        fp4_err32<WMSE, false>(v, w, t.y, F1, unused);
+                        fp4_err32<WMSE, false>(v, b, t.y, F1, unused);
                         keep_best(ok1 ? F1 * t.z : __builtin_huge_valf(), c, e1, e2, cb);
                     }
                 }
-                // |binary64 error - estimate| <= T(estimate): 5u|y| per element
-                // from the shortened arithmetic, summed by Cauchy-Schwarz, plus
-                // the binary32 accumulation; constants carry >= 50% slack
-                const float A = __builtin_fmaxf(a, 6.0f * tab[clamp_pattern((int)sb + hi)].x) * (1.0f + 4.0f * u);
+                // |binary64 error / S^2 - estimate| <= T(estimate): a few u
+                // relative per element from the shortened arithmetic (products
+                // b*y formed from the rounded y), summed by Cauchy-Schwarz, plus
+                // the binary32 accumulation and the gap between fl(s S)^2 and
+                // s^2 S^2.  A bounds |x| / S and 6 D / S over the window;
+                // underflow of y or b*y adds at most 2^-149 per element, which
+                // the A-term covers whenever W > 0 (W == 0 gives exact ties,
+                // never certified).  The constants carry >= 40% slack.
+                const float A = __builtin_fmaxf(a * invS * (1.0f + 4.0f * u),
+                                                6.0f * e4m3_value((uint32_t)clamp_pattern((int)sb + hi))) *
+                                (1.0f + 4.0f * u);
                 const float tail = 64.0f * u * u * A * A * W;
                 const float s1 = __builtin_amdgcn_sqrtf(W * e1) * 1.0001f;
                 const float s2 = __builtin_amdgcn_sqrtf(W * e2) * 1.0001f;

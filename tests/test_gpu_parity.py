@@ -108,6 +108,18 @@ def test_sweep_windows(B, ref, window):
     run_case(B, ref, "nvfp4", 1, 0, 0, x, imp, window=window)
 
 
+@pytest.mark.parametrize("scale", [1e-15, 1e-19, 1e-21, 1e-24, 1e-30, 1e-36, 1e12, 1e30])
+def test_sweep_extreme_magnitudes(B, ref, scale):
+    # global scales whose squared steps fall below (or near the top of) the
+    # binary32 range, and importance weights spread over ~17 decades
+    rng = np.random.default_rng(int(-np.log10(scale)) + 100)
+    x = (rng.standard_t(4, (13, 256)) * scale).astype(np.float32)
+    imp = rng.lognormal(0, 4, 256).astype(np.float32)
+    for obj, window in ((0, (-3, 7)), (1, (-8, 7)), (1, (-2, 9))):
+        run_case(B, ref, "nvfp4", 1, obj, 0, x, imp, window=window)
+    run_case(B, ref, "nvfp4", 1, 1, 16, synth.f32_to_bf16_bits(x), imp)
+
+
 def test_given_global_scale(B, ref):
     x, imp = inputs("f32", 12, 256, seed=8)
     run_case(B, ref, "nvfp4", 1, 1, 0, x, imp, given=0.0625)
