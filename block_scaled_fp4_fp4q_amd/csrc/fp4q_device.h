@@ -131,7 +131,8 @@ __device__ __forceinline__ void fp4_unpack2_scaled(uint32_t packed, float& a, fl
 // nibble of byte k
 __device__ __forceinline__ uint2 fp4_encode16(const float* v, float r)
 {
-    uint32_t lo = 0, hi = 0;
+    // every byte of both words is written: start from any value
+    uint32_t lo = __builtin_nondeterministic_value(0u), hi = __builtin_nondeterministic_value(0u);
     lo = fp4_pack2<0>(lo, v[0] * r, v[1] * r);
     lo = fp4_pack2<1>(lo, v[2] * r, v[3] * r);
     lo = fp4_pack2<2>(lo, v[4] * r, v[5] * r);

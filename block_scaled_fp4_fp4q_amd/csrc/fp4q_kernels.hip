@@ -265,8 +265,12 @@ __global__ __launch_bounds__(kThreads) void nvfp4_absmax(
 // power-of-two scale 2 exactly, so one multiply serves both candidates.
 // With weights, b holds sqrt(w) and each term is formed as (b y - b q)^2, so
 // that the product b y serves both candidates of a pair as well.
+// The code words cw[] are scratch that every call overwrites completely;
+// carrying them from one candidate to the next lets each conversion reuse the
+// previous candidate's dead word instead of copying a fresh one.
 template <bool WMSE, bool PAIR>
-__device__ __forceinline__ void fp4_err32(const float* v, const float* b, float r, float& F1, float& F2)
+__device__ __forceinline__ void fp4_err32(const float* v, const float* b, float r, float& F1, float& F2,
+                                          uint32_t (&cw)[4])
 {
     F1 = 0.0f;
     F2 = 0.0f;
@@ -276,7 +280,7 @@ __device__ __forceinline__ void fp4_err32(const float* v, const float* b, float 
 #pragma unroll
         for (int j = 0; j < 8; ++j)
             y[j] = v[8 * g + j] * r;
-        uint32_t c = 0, c2 = 0;
+        uint32_t c = cw[g], c2 = cw[2 + g];
         c = fp4_pack2<0>(c, y[0], y[1]);
         c = fp4_pack2<1>(c, y[2], y[3]);
         c = fp4_pack2<2>(c, y[4], y[5]);
@@ -295,6 +299,8 @@ __device__ __forceinline__ void fp4_err32(const float* v, const float* b, float 
             fp4_unpack2_scaled<2>(c2, h[4], h[5], 2.0f);
             fp4_unpack2_scaled<3>(c2, h[6], h[7], 2.0f);
         }
+        cw[g] = c;
+        cw[2 + g] = c2;
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
             if constexpr (WMSE) {
@@ -331,28 +337,45 @@ __device__ __forceinline__ void keep_best(float E, int c, float& e1, float& e2, 
     e1 = better ? E : e1;
 }
 
+// keep the two least of non-negative estimates whose low four mantissa bits
+// carry the window offset: as unsigned integers such patterns order like the
+// values (+inf and NaN from overflow order last), and the offset moves each
+// estimate by at most 15 ulp (30u relative)
+__device__ __forceinline__ void keep_best_packed(float E, uint32_t k, uint32_t& p1, uint32_t& p2)
+{
+    const uint32_t p = (__float_as_uint(E) & ~0xFu) | k;
+    const uint32_t hi = p1 > p ? p1 : p; // p1 <= p2 throughout
+    p2 = p2 < hi ? p2 : hi;
+    p1 = p1 < p ? p1 : p;
+}
+
 // the whole window [LO, HI] known at compile time, every pattern sb+k normal
 // and finite, and every pair (k, k+8) an exact doubling: fully unrolled, no
-// clamps or masks (evaluation order differs from ascending k, which only
-// matters for exact ties, and those are never certified)
+// clamps or masks.  Returns the two least packed estimates (see above); only
+// a strict gap beyond the error bounds is certified, so the order among
+// near-equal estimates never decides a result.
 template <bool WMSE, int LO, int HI>
 __device__ __forceinline__ void sweep_fixed(const float* v, const float* b, const float4* tab, int sb,
-                                            float& e1, float& e2, int& cb)
+                                            uint32_t& p1, uint32_t& p2)
 {
+    static_assert(HI - LO < 16, "the window offset must fit in four bits");
+    uint32_t cw[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        cw[i] = __builtin_nondeterministic_value(0u);
 #pragma unroll
     for (int k = LO; k <= HI; ++k) {
         if (((k - LO) & 15) >= 8)
             continue; // evaluated with its partner k-8
-        const int c = sb + k;
-        const float4 t = tab[c];
+        const float4 t = tab[sb + k];
         float F1, F2;
         if (k + 8 <= HI) {
-            fp4_err32<WMSE, true>(v, b, t.y, F1, F2);
-            keep_best(F1 * t.z, c, e1, e2, cb);
-            keep_best(F2 * t.z, c + 8, e1, e2, cb);
+            fp4_err32<WMSE, true>(v, b, t.y, F1, F2, cw);
+            keep_best_packed(F1 * t.z, (uint32_t)(k - LO), p1, p2);
+            keep_best_packed(F2 * t.z, (uint32_t)(k + 8 - LO), p1, p2);
         } else {
-            fp4_err32<WMSE, false>(v, b, t.y, F1, F2);
-            keep_best(F1 * t.z, c, e1, e2, cb);
+            fp4_err32<WMSE, false>(v, b, t.y, F1, F2, cw);
+            keep_best_packed(F1 * t.z, (uint32_t)(k - LO), p1, p2);
         }
     }
 }
@@ -511,37 +534,46 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
                 }
                 float e1 = __builtin_huge_valf(), e2 = __builtin_huge_valf();
                 int cb = 1;
+                float rel = 32.0f * u; // relative part of the bound
                 const bool interior = WIN != 0 && pairs_exact && (int)sb + FLO >= 8 && (int)sb + FHI <= 0x7E;
                 if (WIN != 0 && __builtin_amdgcn_ballot_w64(!interior) == 0) {
-                    sweep_fixed<WMSE, FLO, FHI>(v, b, tab, (int)sb, e1, e2, cb);
-                } else
-                // offsets k and k+8 pair up in runs of eight; the rest are singles
-                for (int k = lo; k <= hi; ++k) {
-                    if (((k - lo) & 15) >= 8)
-                        continue; // evaluated with its partner k-8 (uniform branch)
-                    const bool ok1 = k >= klo && k <= khi;
-                    const int c = clamp_pattern((int)sb + k);
-                    const float4 t = tab[c];
-                    if (k + 8 <= hi) {
-                        const bool ok2 = k + 8 >= klo && k + 8 <= khi;
-                        const int c8 = clamp_pattern((int)sb + k + 8);
-                        float F1, F2, E2;
-                        if (__builtin_amdgcn_ballot_w64(t.w == 0.0f) == 0) {
-                            // every lane's pair is an exact doubling: shared product
-                            fp4_err32<WMSE, true>(v, b, t.y, F1, F2);
-                            E2 = F2 * t.z;
+                    uint32_t p1 = 0x7F800000u, p2 = 0x7F800000u;
+                    sweep_fixed<WMSE, FLO, FHI>(v, b, tab, (int)sb, p1, p2);
+                    // an overflowed estimate (pattern >= +inf) is never certified
+                    e1 = p1 < 0x7F800000u ? __uint_as_float(p1) : __builtin_huge_valf();
+                    e2 = p2 < 0x7F800000u ? __uint_as_float(p2) : __builtin_huge_valf();
+                    cb = (int)sb + FLO + (int)(p1 & 0xFu);
+                    rel = 64.0f * u; // + 30u from the packed offsets
+                } else {
+                    uint32_t cw[4] = {0u, 0u, 0u, 0u};
+                    // offsets k and k+8 pair up in runs of eight; the rest are singles
+                    for (int k = lo; k <= hi; ++k) {
+                        if (((k - lo) & 15) >= 8)
+                            continue; // evaluated with its partner k-8 (uniform branch)
+                        const bool ok1 = k >= klo && k <= khi;
+                        const int c = clamp_pattern((int)sb + k);
+                        const float4 t = tab[c];
+                        if (k + 8 <= hi) {
+                            const bool ok2 = k + 8 >= klo && k + 8 <= khi;
+                            const int c8 = clamp_pattern((int)sb + k + 8);
+                            float F1, F2, E2;
+                            if (__builtin_amdgcn_ballot_w64(t.w == 0.0f) == 0) {
+                                // every lane's pair is an exact doubling: shared product
+                                fp4_err32<WMSE, true>(v, b, t.y, F1, F2, cw);
+                                E2 = F2 * t.z;
+                            } else {
+                                float unused;
+                                fp4_err32<WMSE, false>(v, b, t.y, F1, unused, cw);
+                                fp4_err32<WMSE, false>(v, b, tab[c8].y, F2, unused, cw);
+                                E2 = F2 * tab[c8].z;
+                            }
+                            keep_best(ok1 ? F1 * t.z : __builtin_huge_valf(), c, e1, e2, cb);
+                            keep_best(ok2 ? E2 : __builtin_huge_valf(), c8, e1, e2, cb);
                         } else {
-                            float unused;
-                            fp4_err32<WMSE, false>(v, b, t.y, F1, unused);
-                            fp4_err32<WMSE, false>(v, b, tab[c8].y, F2, unused);
-                            E2 = F2 * tab[c8].z;
+                            float F1, unused;
+                            fp4_err32<WMSE, false>(v, b, t.y, F1, unused, cw);
+                            keep_best(ok1 ? F1 * t.z : __builtin_huge_valf(), c, e1, e2, cb);
                         }
-                        keep_best(ok1 ? F1 * t.z : __builtin_huge_valf(), c, e1, e2, cb);
-                        keep_best(ok2 ? E2 : __builtin_huge_valf(), c8, e1, e2, cb);
-                    } else {
-                        float F1, unused;
-                        fp4_err32<WMSE, false>(v, b, t.y, F1, unused);
-                        keep_best(ok1 ? F1 * t.z : __builtin_huge_valf(), c, e1, e2, cb);
                     }
                 }
                 // |binary64 error / S^2 - estimate| <= T(estimate): a few u
@@ -558,9 +590,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
                 const float tail = 64.0f * u * u * A * A * W;
                 const float s1 = __builtin_amdgcn_sqrtf(W * e1) * 1.0001f;
                 const float s2 = __builtin_amdgcn_sqrtf(W * e2) * 1.0001f;
-                const float t1 = 16.0f * u * A * s1 + 32.0f * u * e1 + tail;
-                const float t2 = 16.0f * u * A * s2 + 32.0f * u * e2 + tail;
-                const bool certain = klo <= khi && e1 < __builtin_huge_valf() &&
+                const float t1 = 16.0f * u * A * s1 + rel * e1 + tail;
+                const float t2 = 16.0f * u * A * s2 + rel * e2 + tail;
+                // 6 D of the window's top pattern finite: no candidate's
+                // reconstruction overflows (the exact path handles those)
+                const bool finite_top = 6.0f * tab[clamp_pattern((int)sb + hi)].x < __builtin_huge_valf();
+                const bool certain = klo <= khi && finite_top && e1 < __builtin_huge_valf() &&
                                      ((e2 == __builtin_huge_valf()) || (e2 - t2 > e1 + t1));
                 if (certain) {
                     codes[blk] = fp4_encode16(v, tab[cb].y);

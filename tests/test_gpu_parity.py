@@ -120,6 +120,17 @@ def test_sweep_extreme_magnitudes(B, ref, scale):
     run_case(B, ref, "nvfp4", 1, 1, 16, synth.f32_to_bf16_bits(x), imp)
 
 
+def test_sweep_near_float_max(B, ref):
+    # max|x| = 3e38: the top patterns' reconstructions 6 D overflow to inf,
+    # which the exact errors see and a binary32 estimate in step units does not
+    rng = np.random.default_rng(7)
+    x = rng.standard_t(4, (11, 128))
+    x = (x / np.abs(x).max() * 3.0e38).astype(np.float32)
+    imp = rng.lognormal(0, 1, 128).astype(np.float32)
+    for obj, window in ((0, (-3, 7)), (1, (-8, 7))):
+        run_case(B, ref, "nvfp4", 1, obj, 0, x, imp, window=window)
+
+
 def test_given_global_scale(B, ref):
     x, imp = inputs("f32", 12, 256, seed=8)
     run_case(B, ref, "nvfp4", 1, 1, 0, x, imp, given=0.0625)
