@@ -1031,39 +1031,63 @@ __device__ __forceinline__ void load_codes(const uint8_t* __restrict__ codes, in
     }
 }
 
+// One lane decodes one block; each wave then writes its 64 consecutive
+// blocks' output as whole 16-byte chunks in lane order (1 KiB contiguous per
+// store instruction) after passing them through LDS, instead of every lane
+// storing its own 32-128 bytes with a stride across the wave.
 template <int FMT, int B, bool ROT, bool OUT_BF16>
 __global__ __launch_bounds__(kThreads) void dequant(
     const uint8_t* __restrict__ codes, const uint8_t* __restrict__ scales,
     const float* __restrict__ Sp, int64_t nblocks, void* __restrict__ y)
 {
+    constexpr int NQ = B * (OUT_BF16 ? 2 : 4) / 16; // 16-byte output chunks per block
+    __shared__ u32x4 stage[kThreads / 64][64 * NQ];
+    const int lane = threadIdx.x & 63;
+    u32x4* st = stage[threadIdx.x >> 6];
     const float S = (FMT == kMXFP4) ? 1.0f : *Sp;
-    for (int64_t blk = (int64_t)blockIdx.x * kThreads + threadIdx.x; blk < nblocks;
-         blk += (int64_t)gridDim.x * kThreads) {
-        uint32_t wds[B / 8];
-        load_codes<B>(codes, blk, wds);
-        float o[B];
-        decode_block<FMT, B>(wds, scales[blk], S, o);
-        if constexpr (ROT)
-            fwht<B>(o);
-        if constexpr (OUT_BF16) {
-            u32x4* p = reinterpret_cast<u32x4*>(y) + blk * (B / 8);
+    const int64_t stride = (int64_t)gridDim.x * kThreads;
+    // wave-uniform loop: base is this wave's first block
+    for (int64_t base = (int64_t)blockIdx.x * kThreads + (threadIdx.x & ~63); base < nblocks; base += stride) {
+        const int64_t blk = base + lane;
+        if (blk < nblocks) {
+            uint32_t wds[B / 8];
+            load_codes<B>(codes, blk, wds);
+            float o[B];
+            decode_block<FMT, B>(wds, scales[blk], S, o);
+            if constexpr (ROT)
+                fwht<B>(o);
 #pragma unroll
-            for (int q = 0; q < B / 8; ++q) {
+            for (int q = 0; q < NQ; ++q) {
                 u32x4 t;
-                t.x = bf16_pair(o[8 * q + 0], o[8 * q + 1]);
-                t.y = bf16_pair(o[8 * q + 2], o[8 * q + 3]);
-                t.z = bf16_pair(o[8 * q + 4], o[8 * q + 5]);
-                t.w = bf16_pair(o[8 * q + 6], o[8 * q + 7]);
-                __builtin_nontemporal_store(t, p + q);
-            }
-        } else {
-            f32x4* p = reinterpret_cast<f32x4*>(y) + blk * (B / 4);
-#pragma unroll
-            for (int q = 0; q < B / 4; ++q) {
-                const f32x4 t = {o[4 * q], o[4 * q + 1], o[4 * q + 2], o[4 * q + 3]};
-                __builtin_nontemporal_store(t, p + q);
+                if constexpr (OUT_BF16) {
+                    t.x = bf16_pair(o[8 * q + 0], o[8 * q + 1]);
+                    t.y = bf16_pair(o[8 * q + 2], o[8 * q + 3]);
+                    t.z = bf16_pair(o[8 * q + 4], o[8 * q + 5]);
+                    t.w = bf16_pair(o[8 * q + 6], o[8 * q + 7]);
+                } else {
+                    t.x = __float_as_uint(o[4 * q + 0]);
+                    t.y = __float_as_uint(o[4 * q + 1]);
+                    t.z = __float_as_uint(o[4 * q + 2]);
+                    t.w = __float_as_uint(o[4 * q + 3]);
+                }
+                st[lane * NQ + q] = t;
             }
         }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        const int64_t left = nblocks - base;
+        const int nch = (left < 64 ? (int)left : 64) * NQ; // chunks of this wave's blocks
+        u32x4* out = reinterpret_cast<u32x4*>(y) + base * NQ;
+#pragma unroll
+        for (int q = 0; q < NQ; ++q) {
+            const int ch = q * 64 + lane;
+            if (ch < nch)
+                __builtin_nontemporal_store(st[ch], out + ch);
+        }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     }
 }
 
