@@ -214,6 +214,103 @@ __device__ __forceinline__ void load_weights16(const float* __restrict__ imp, in
     }
 }
 
+// ---- importance square roots -------------------------------------------------
+
+constexpr int kRootCols = 4096; // importance columns whose square roots fit in LDS
+
+// sqrt(w) of every column and the weight sum of every 16 columns, into LDS,
+// when there are at most kRootCols columns; returns whether it did (the
+// caller synchronizes the workgroup before use)
+__device__ __forceinline__ bool roots_prologue(const float* __restrict__ imp, int64_t cols,
+                                               float* root, float* wsum)
+{
+    if (cols > kRootCols)
+        return false;
+    for (int j = threadIdx.x; j < (int)cols; j += kThreads)
+        root[j] = __builtin_sqrtf(imp[j]);
+    for (int j = threadIdx.x; j < (int)(cols / 16); j += kThreads) {
+        float W = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+            W += imp[16 * j + i];
+        wsum[j] = W;
+    }
+    return true;
+}
+
+// b = sqrt(w) of the N columns from col0 (a multiple of 16) and their weight
+// sum W (rounded: the bounds carry slack for it)
+template <int N>
+__device__ __forceinline__ void block_roots(const float* __restrict__ imp, const float* root,
+                                            const float* wsum, bool in_lds, int64_t col0, float* b,
+                                            float& W)
+{
+    if (in_lds) {
+        const float4* rp = reinterpret_cast<const float4*>(root + col0);
+#pragma unroll
+        for (int q = 0; q < N / 4; ++q) {
+            const float4 t = rp[q];
+            b[4 * q + 0] = t.x; b[4 * q + 1] = t.y; b[4 * q + 2] = t.z; b[4 * q + 3] = t.w;
+        }
+        W = wsum[col0 / 16];
+        if constexpr (N == 32)
+            W += wsum[col0 / 16 + 1];
+    } else {
+#pragma unroll
+        for (int q = 0; q < N / 16; ++q)
+            load_weights16(imp, col0 + 16 * q, b + 16 * q);
+        W = 0.0f;
+#pragma unroll
+        for (int i = 0; i < N; ++i) {
+            W += b[i];
+            b[i] = __builtin_sqrtf(b[i]);
+        }
+    }
+}
+
+// ---- certified binary32 estimates ------------------------------------------
+//
+// A candidate's block error is estimated in binary32 in units of a fixed step
+// (S^2 for E4M3 scales, the lowest step^2 for E8M0 windows): the conversion
+// gives the method's own codes, and each term is (b y - b q)^2 with
+// b = sqrt(w) (or (y - q)^2).  The binary64 error then lies within
+// est_bound(estimate) of the estimate, where A bounds |x| and 6 D (7 D_int)
+// over the candidates and W the weight sum, all in the same units, and rel
+// the relative part (derivation at the ScaleSweep kernel).
+
+__device__ __forceinline__ float est_bound(float E, float A, float W, float rel)
+{
+    constexpr float u = 0x1p-24f;
+    return 16.0f * u * A * __builtin_amdgcn_sqrtf(W * E) * 1.0001f + rel * E + 64.0f * u * u * A * A * W;
+}
+
+// INT4 estimate of IF4's 6/7 method in units of the INT4 step: q =
+// min(RNE(fl(|x| ri)), 7), exactly the method's integer
+template <bool WMSE>
+__device__ __forceinline__ float int4_est16(const float* v, const float* b, float ri)
+{
+    float F = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        const float z = __builtin_fabsf(v[i]) * ri;
+        const float q = __builtin_fminf(__builtin_rintf(z), 7.0f);
+        float d;
+        if constexpr (WMSE)
+            d = __builtin_fmaf(-b[i], q, b[i] * z);
+        else
+            d = z - q;
+        F = __builtin_fmaf(d, d, F);
+    }
+    return F;
+}
+
+// the 32 sign|magnitude nibbles of E2M1(v[i] * r) (hardware conversion)
+__device__ __forceinline__ uint4 fp4_encode32(const float* v, float r)
+{
+    const uint2 lo = fp4_encode16(v, r), hi = fp4_encode16(v + 16, r);
+    return make_uint4(lo.x, lo.y, hi.x, hi.y);
+}
+
 // ---------------------------------------------------------------------------
 // NVFP4 AbsMax
 // ---------------------------------------------------------------------------
@@ -381,7 +478,6 @@ __device__ __forceinline__ void sweep_fixed(const float* v, const float* b, cons
 }
 
 constexpr int kQueueCap = 1024; // fallback queue entries per workgroup (LDS)
-constexpr int kRootCols = 4096; // importance columns whose square roots fit in LDS
 
 template <bool BF16, bool ROT, bool WMSE, int WIN>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) void nvfp4_sweep(
@@ -407,21 +503,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
         const bool twice = c >= 8 && c + 8 <= 0x7E && D8 == 2.0f * D && (1.0f / D8) == 0.5f * (1.0f / D);
         tab[c] = make_float4(D, 1.0f / D, sc * sc, twice ? 1.0f : 0.0f);
     }
-    const int64_t cols = blocks_per_row * 16;
-    const bool roots_in_lds = WMSE && cols <= kRootCols;
-    if constexpr (WMSE) {
-        if (roots_in_lds) {
-            for (int j = threadIdx.x; j < (int)cols; j += kThreads)
-                root[j] = __builtin_sqrtf(imp[j]);
-            for (int j = threadIdx.x; j < (int)blocks_per_row; j += kThreads) {
-                float W = 0.0f;
-#pragma unroll
-                for (int i = 0; i < 16; ++i)
-                    W += imp[16 * j + i];
-                wsum[j] = W;
-            }
-        }
-    }
+    bool roots_in_lds = false;
+    if constexpr (WMSE)
+        roots_in_lds = roots_prologue(imp, blocks_per_row * 16, root, wsum);
     if (threadIdx.x == 0)
         qn = 0;
     __syncthreads();
@@ -513,25 +597,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
                 const int klo = max(lo, 1 - (int)sb), khi = min(hi, 0x7E - (int)sb);
                 float b[16];
                 float W = 16.0f;
-                if constexpr (WMSE) {
-                    if (roots_in_lds) {
-                        const float4* rp = reinterpret_cast<const float4*>(root + col * 16);
-#pragma unroll
-                        for (int q = 0; q < 4; ++q) {
-                            const float4 t = rp[q];
-                            b[4 * q + 0] = t.x; b[4 * q + 1] = t.y; b[4 * q + 2] = t.z; b[4 * q + 3] = t.w;
-                        }
-                        W = wsum[col];
-                    } else {
-                        load_weights16(imp, col * 16, b);
-                        W = 0.0f;
-#pragma unroll
-                        for (int i = 0; i < 16; ++i) {
-                            W += b[i];
-                            b[i] = __builtin_sqrtf(b[i]);
-                        }
-                    }
-                }
+                if constexpr (WMSE)
+                    block_roots<16>(imp, root, wsum, roots_in_lds, col * 16, b, W);
                 float e1 = __builtin_huge_valf(), e2 = __builtin_huge_valf();
                 int cb = 1;
                 float rel = 32.0f * u; // relative part of the bound
@@ -632,8 +699,15 @@ __global__ __launch_bounds__(kThreads) void if4_quant(
     const float* __restrict__ imp, const float* __restrict__ partials, int npart,
     float* __restrict__ Sp, uint2* __restrict__ codes, uint8_t* __restrict__ scales)
 {
+    __shared__ float root[WMSE ? kRootCols : 1];
+    __shared__ float wsum[WMSE ? kRootCols / 16 : 1];
     const float S = global_scale(partials, npart, Sp);
-    const float S6 = 6.0f * S;
+    bool roots_in_lds = false;
+    if constexpr (WMSE)
+        roots_in_lds = roots_prologue(imp, blocks_per_row * 16, root, wsum);
+    __syncthreads();
+    const float S6 = 6.0f * S, invS = 1.0f / S;
+    constexpr float u = 0x1p-24f;
     for (int64_t blk = (int64_t)blockIdx.x * kThreads + threadIdx.x; blk < nblocks;
          blk += (int64_t)gridDim.x * kThreads) {
         float v[16];
@@ -649,16 +723,44 @@ __global__ __launch_bounds__(kThreads) void if4_quant(
         } else {
             uint32_t sb = e4m3_round(a / S6);
             sb = sb < 1u ? 1u : sb;
-            float w[16];
-            if constexpr (WMSE)
-                load_weights16(imp, (blk % blocks_per_row) * 16, w);
-            const float D = e4m3_value(sb) * S;
+            const int64_t col0 = (blk % blocks_per_row) * 16;
+            const float sv = e4m3_value(sb);
+            const float D = sv * S;
             const float r = 1.0f / D;
             const float Di = D * kInt4Step;
             const float ri = 1.0f / Di;
-            const double ef = fp4_error16<WMSE>(v, w, D, r);
-            const double ei = int4_error16<WMSE>(v, w, Di, ri);
-            if (ei < ef) {
+            // binary32 estimates in units of S^2, certified when separated
+            // by more than their bounds (INT4 must be strictly lower)
+            float b[16];
+            float W = 16.0f;
+            if constexpr (WMSE)
+                block_roots<16>(imp, root, wsum, roots_in_lds, col0, b, W);
+            uint32_t cw[4] = {0u, 0u, 0u, 0u};
+            float Ff, unused;
+            fp4_err32<WMSE, false>(v, b, r, Ff, unused, cw);
+            const float Fi = int4_est16<WMSE>(v, b, ri);
+            const float sz = sv * kInt4Step;
+            const float Ef = Ff * (sv * sv), Ei = Fi * (sz * sz);
+            const float A = __builtin_fmaxf(a * invS * (1.0f + 4.0f * u), 6.0f * sv) * (1.0f + 4.0f * u);
+            const float Tf = est_bound(Ef, A, W, 40.0f * u), Ti = est_bound(Ei, A, W, 40.0f * u);
+            // reconstructions 6 D and 7 D_int finite (the exact path sees overflow)
+            const bool finite = 6.0f * D < __builtin_huge_valf() && 7.0f * Di < __builtin_huge_valf();
+            int choice = -1; // 0 FP4, 1 INT4, -1 undecided
+            if (finite) {
+                if (Ei + Ti < Ef - Tf)
+                    choice = 1;
+                else if (Ef + Tf <= Ei - Ti)
+                    choice = 0;
+            }
+            if (choice < 0) { // exact binary64 comparison
+                float w[16];
+                if constexpr (WMSE)
+                    load_weights16(imp, col0, w);
+                const double ef = fp4_error16<WMSE>(v, w, D, r);
+                const double ei = int4_error16<WMSE>(v, w, Di, ri);
+                choice = ei < ef ? 1 : 0;
+            }
+            if (choice == 1) {
                 sbyte = sb | 0x80u;
                 packed = encode16_int4(v, ri);
             } else {
@@ -697,15 +799,10 @@ __global__ __launch_bounds__(kThreads) void mxfp4_quant(
         const float a = block_absmax<32>(v);
         int e = (a == 0.0f) ? -127 : floor_log2_f32(a) - 2;
         e = e < -127 ? -127 : (e > 127 ? 127 : e);
-        const float r = __uint_as_float((uint32_t)(127 - e) << 23); // 2^-e, -e <= 127
-        uint32_t wds[4] = {0, 0, 0, 0};
-#pragma unroll
-        for (int i = 0; i < 32; ++i) {
-            const uint32_t sgn = __float_as_uint(v[i]) >> 31;
-            const float q = e2m1_q(__builtin_fabsf(v[i]) * r);
-            wds[i >> 3] |= ((sgn << 3) | e2m1_code(q)) << (4 * (i & 7));
-        }
-        codes[blk] = make_uint4(wds[0], wds[1], wds[2], wds[3]);
+        // 2^-e exactly (a finite maximum gives e <= 125), so |v| 2^-e is the
+        // method's own product and the hardware conversion its own code
+        const float r = __uint_as_float((uint32_t)(127 - e) << 23);
+        codes[blk] = fp4_encode32(v, r);
         scales[blk] = (uint8_t)(e + 127);
     }
 }
@@ -721,20 +818,6 @@ __device__ __forceinline__ int mx_exponent(float a)
 {
     const int e = (a == 0.0f) ? -127 : floor_log2_f32(a) - 2;
     return e < -127 ? -127 : (e > 127 ? 127 : e);
-}
-
-// the 32 nibbles of E2M1(|v| 2^-e) with signs
-__device__ __forceinline__ uint4 mx_encode32(const float* v, int e)
-{
-    const float r = pow2f(-e);
-    uint32_t wds[4] = {0, 0, 0, 0};
-#pragma unroll
-    for (int i = 0; i < 32; ++i) {
-        const uint32_t sgn = __float_as_uint(v[i]) >> 31;
-        const float q = e2m1_q(__builtin_fabsf(v[i]) * r);
-        wds[i >> 3] |= ((sgn << 3) | e2m1_code(q)) << (4 * (i & 7));
-    }
-    return make_uint4(wds[0], wds[1], wds[2], wds[3]);
 }
 
 // binary64 block error of the MXFP4 encoding with exponent e
@@ -762,57 +845,142 @@ __device__ __forceinline__ void load_weights32(const float* __restrict__ imp, in
     load_weights16(imp, col0 + 16, w + 16);
 }
 
+// binary32 estimate of the MXFP4 error at exponent e_lo + j in units of
+// 2^(2 e_lo): y = v 2^-e_lo is exact, the conversion with scale P = 2^j gives
+// the codes of y / P and the decode with the same scale P q, exactly
+template <bool WMSE>
+__device__ __forceinline__ float mx_est32(const float* y, const float* by, const float* b, float P,
+                                          uint32_t (&cw)[4])
+{
+    float F = 0.0f;
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+        uint32_t c = cw[g];
+        c = fp4_pack2_scaled<0>(c, y[8 * g + 0], y[8 * g + 1], P);
+        c = fp4_pack2_scaled<1>(c, y[8 * g + 2], y[8 * g + 3], P);
+        c = fp4_pack2_scaled<2>(c, y[8 * g + 4], y[8 * g + 5], P);
+        c = fp4_pack2_scaled<3>(c, y[8 * g + 6], y[8 * g + 7], P);
+        float q[8];
+        fp4_unpack2_scaled<0>(c, q[0], q[1], P);
+        fp4_unpack2_scaled<1>(c, q[2], q[3], P);
+        fp4_unpack2_scaled<2>(c, q[4], q[5], P);
+        fp4_unpack2_scaled<3>(c, q[6], q[7], P);
+        cw[g] = c;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const int i = 8 * g + j;
+            float d;
+            if constexpr (WMSE)
+                d = __builtin_fmaf(-b[i], q[j], by[i]);
+            else
+                d = y[i] - q[j];
+            F = __builtin_fmaf(d, d, F);
+        }
+    }
+    return F;
+}
+
 // MXFP4 with a window of E8M0 exponents around the OCP one, binary64 argmin
 // (first least in ascending exponent) -- "Bridging the Gap ... Microscaling
-// FP4" page, Method 2: format-specific scale search for E8M0
+// FP4" page, Method 2: format-specific scale search for E8M0.  Windows of at
+// most 16 unclamped exponents take certified binary32 estimates; the rest,
+// and every block they leave undecided, the exact binary64 search.
 template <bool BF16, bool ROT, bool WMSE>
 __global__ __launch_bounds__(kThreads) void mxfp4_sweep(
     const void* __restrict__ x, int64_t nblocks, int64_t blocks_per_row,
     const float* __restrict__ imp, int lo, int hi, uint4* __restrict__ codes,
     uint8_t* __restrict__ scales)
 {
+    __shared__ float root[WMSE ? kRootCols : 1];
+    __shared__ float wsum[WMSE ? kRootCols / 16 : 1];
+    bool roots_in_lds = false;
+    if constexpr (WMSE)
+        roots_in_lds = roots_prologue(imp, blocks_per_row * 32, root, wsum);
+    __syncthreads();
+    constexpr float u = 0x1p-24f;
+    const int K = hi - lo + 1;
     for (int64_t blk = (int64_t)blockIdx.x * kThreads + threadIdx.x; blk < nblocks;
          blk += (int64_t)gridDim.x * kThreads) {
         float v[32];
         load_block<32, BF16>(x, blk, v);
         if constexpr (ROT)
             fwht<32>(v);
-        const int e0 = mx_exponent(block_absmax<32>(v));
-        float w[32];
-        if constexpr (WMSE)
-            load_weights32(imp, (blk % blocks_per_row) * 32, w);
-        // the first candidate is taken unconditionally, so that a window
-        // whose every error overflows still keeps its first exponent
-        double best = 0.0;
-        int eb = e0, eprev = 1000;
-        for (int k = lo; k <= hi; ++k) {
-            int e = e0 + k;
-            e = e < -127 ? -127 : (e > 127 ? 127 : e);
-            if (e == eprev)
-                continue;
-            const double E = mx_error32<WMSE>(v, w, e);
-            if (eprev == 1000 || E < best) {
-                best = E;
-                eb = e;
+        const float a = block_absmax<32>(v);
+        const int e0 = mx_exponent(a);
+        const int64_t col0 = (blk % blocks_per_row) * 32;
+        int eb = 1000; // chosen exponent; 1000 = undecided
+        // fast path: no clamping, and 6 * 2^e of the top exponent finite
+        if (a != 0.0f && K <= 16 && e0 + lo >= -127 && e0 + hi <= 125) {
+            const int el = e0 + lo;
+            const float rl = pow2f(-el);
+            float y[32], b[32], by[32];
+            float W = 32.0f;
+#pragma unroll
+            for (int i = 0; i < 32; ++i)
+                y[i] = v[i] * rl;
+            if constexpr (WMSE) {
+                block_roots<32>(imp, root, wsum, roots_in_lds, col0, b, W);
+#pragma unroll
+                for (int i = 0; i < 32; ++i)
+                    by[i] = b[i] * y[i];
             }
-            eprev = e;
+            uint32_t cw[4] = {0u, 0u, 0u, 0u};
+            float e1 = __builtin_huge_valf(), e2 = __builtin_huge_valf();
+            int jb = 0;
+            float P = 1.0f;
+            for (int j = 0; j < K; ++j, P *= 2.0f) {
+                const float E = mx_est32<WMSE>(y, by, b, P, cw);
+                keep_best(E, j, e1, e2, jb);
+            }
+            const float A = __builtin_fmaxf(a * rl, 6.0f * pow2f(K - 1)) * (1.0f + 4.0f * u);
+            const float t1 = est_bound(e1, A, W, 32.0f * u), t2 = est_bound(e2, A, W, 32.0f * u);
+            if (e1 < __builtin_huge_valf() && (K == 1 || e2 - t2 > e1 + t1))
+                eb = el + jb;
         }
-        codes[blk] = mx_encode32(v, eb);
+        if (eb == 1000) { // exact binary64 search over the clamped window
+            float w[32];
+            if constexpr (WMSE)
+                load_weights32(imp, col0, w);
+            double best = 0.0;
+            int eprev = 1000;
+            eb = e0;
+            for (int k = lo; k <= hi; ++k) {
+                int e = e0 + k;
+                e = e < -127 ? -127 : (e > 127 ? 127 : e);
+                if (e == eprev)
+                    continue;
+                const double E = mx_error32<WMSE>(v, w, e);
+                if (eprev == 1000 || E < best) { // the first exponent is always taken
+                    best = E;
+                    eb = e;
+                }
+                eprev = e;
+            }
+        }
+        codes[blk] = fp4_encode32(v, pow2f(-eb));
         scales[blk] = (uint8_t)(eb + 127);
     }
 }
 
 // NVFP4 Four Over Six: the block maximum onto 6 (AbsMax) or onto 4, the
 // lower binary64 error kept, a tie keeps 6 (Adaptive Block-Scaled Data Types
-// page, Problem; ScaleSweep page, Problem definition)
+// page, Problem; ScaleSweep page, Problem definition).  Certified binary32
+// estimates decide when separated; the rest compare exactly.
 template <bool BF16, bool ROT, bool WMSE>
 __global__ __launch_bounds__(kThreads) void nvfp4_foursix(
     const void* __restrict__ x, int64_t nblocks, int64_t blocks_per_row,
     const float* __restrict__ imp, const float* __restrict__ partials, int npart,
     float* __restrict__ Sp, uint2* __restrict__ codes, uint8_t* __restrict__ scales)
 {
+    __shared__ float root[WMSE ? kRootCols : 1];
+    __shared__ float wsum[WMSE ? kRootCols / 16 : 1];
     const float S = global_scale(partials, npart, Sp);
-    const float S6 = 6.0f * S, S4 = 4.0f * S;
+    bool roots_in_lds = false;
+    if constexpr (WMSE)
+        roots_in_lds = roots_prologue(imp, blocks_per_row * 16, root, wsum);
+    __syncthreads();
+    const float S6 = 6.0f * S, S4 = 4.0f * S, invS = 1.0f / S;
+    constexpr float u = 0x1p-24f;
     for (int64_t blk = (int64_t)blockIdx.x * kThreads + threadIdx.x; blk < nblocks;
          blk += (int64_t)gridDim.x * kThreads) {
         float v[16];
@@ -826,15 +994,40 @@ __global__ __launch_bounds__(kThreads) void nvfp4_foursix(
             uint32_t s6 = e4m3_round(a / S6), s4 = e4m3_round(a / S4);
             s6 = s6 < 1u ? 1u : s6;
             s4 = s4 < 1u ? 1u : s4;
-            float w[16];
-            if constexpr (WMSE)
-                load_weights16(imp, (blk % blocks_per_row) * 16, w);
-            const float D6 = e4m3_value(s6) * S, r6 = 1.0f / D6;
+            const float v6 = e4m3_value(s6), v4 = e4m3_value(s4);
+            const float D6 = v6 * S, r6 = 1.0f / D6;
             cb = s6;
             r = r6;
             if (s4 != s6) {
-                const float D4 = e4m3_value(s4) * S, r4 = 1.0f / D4;
-                if (fp4_error16<WMSE>(v, w, D4, r4) < fp4_error16<WMSE>(v, w, D6, r6)) {
+                const int64_t col0 = (blk % blocks_per_row) * 16;
+                const float D4 = v4 * S, r4 = 1.0f / D4;
+                float b[16];
+                float W = 16.0f;
+                if constexpr (WMSE)
+                    block_roots<16>(imp, root, wsum, roots_in_lds, col0, b, W);
+                uint32_t cw[4] = {0u, 0u, 0u, 0u};
+                float F6, F4, unused;
+                fp4_err32<WMSE, false>(v, b, r6, F6, unused, cw);
+                fp4_err32<WMSE, false>(v, b, r4, F4, unused, cw);
+                const float E6 = F6 * (v6 * v6), E4 = F4 * (v4 * v4);
+                const float A = __builtin_fmaxf(a * invS * (1.0f + 4.0f * u), 6.0f * __builtin_fmaxf(v6, v4)) *
+                                (1.0f + 4.0f * u);
+                const float T6 = est_bound(E6, A, W, 32.0f * u), T4 = est_bound(E4, A, W, 32.0f * u);
+                const bool finite = 6.0f * __builtin_fmaxf(D6, D4) < __builtin_huge_valf();
+                int four = -1; // 1: s4 strictly lower, 0: s6 kept, -1 undecided
+                if (finite) {
+                    if (E4 + T4 < E6 - T6)
+                        four = 1;
+                    else if (E6 + T6 <= E4 - T4)
+                        four = 0;
+                }
+                if (four < 0) { // exact binary64 comparison
+                    float w[16];
+                    if constexpr (WMSE)
+                        load_weights16(imp, col0, w);
+                    four = fp4_error16<WMSE>(v, w, D4, r4) < fp4_error16<WMSE>(v, w, D6, r6) ? 1 : 0;
+                }
+                if (four) {
                     cb = s4;
                     r = r4;
                 }
@@ -846,22 +1039,33 @@ __global__ __launch_bounds__(kThreads) void nvfp4_foursix(
 }
 
 // IF4 over a window of patterns: per pattern the FP4 then the INT4 encoding,
-// the first least binary64 error kept
+// the first least binary64 error kept.  Certified binary32 estimates decide
+// when the two least are separated; the rest run the exact search.
 template <bool BF16, bool ROT, bool WMSE>
 __global__ __launch_bounds__(kThreads) void if4_sweep(
     const void* __restrict__ x, int64_t nblocks, int64_t blocks_per_row,
     const float* __restrict__ imp, const float* __restrict__ partials, int npart,
     float* __restrict__ Sp, int lo, int hi, uint2* __restrict__ codes, uint8_t* __restrict__ scales)
 {
-    __shared__ float4 tab[128]; // D, r, D_int = fl32(D 6/7), r_int
+    __shared__ float4 tab[128];  // D, r, D_int = fl32(D 6/7), r_int
+    __shared__ float2 tab2[128]; // s^2 and (s 6/7)^2: the estimates' units over S^2
+    __shared__ float root[WMSE ? kRootCols : 1];
+    __shared__ float wsum[WMSE ? kRootCols / 16 : 1];
     const float S = global_scale(partials, npart, Sp);
     for (int c = threadIdx.x; c < 128; c += kThreads) {
-        const float D = e4m3_value((uint32_t)(c < 0x7E ? c : 0x7E)) * S;
+        const float sv = e4m3_value((uint32_t)(c < 0x7E ? c : 0x7E));
+        const float D = sv * S;
         const float Di = D * kInt4Step;
         tab[c] = make_float4(D, 1.0f / D, Di, 1.0f / Di);
+        const float sz = sv * kInt4Step;
+        tab2[c] = make_float2(sv * sv, sz * sz);
     }
+    bool roots_in_lds = false;
+    if constexpr (WMSE)
+        roots_in_lds = roots_prologue(imp, blocks_per_row * 16, root, wsum);
     __syncthreads();
-    const float S6 = 6.0f * S;
+    const float S6 = 6.0f * S, invS = 1.0f / S;
+    constexpr float u = 0x1p-24f;
     for (int64_t blk = (int64_t)blockIdx.x * kThreads + threadIdx.x; blk < nblocks;
          blk += (int64_t)gridDim.x * kThreads) {
         float v[16];
@@ -876,27 +1080,59 @@ __global__ __launch_bounds__(kThreads) void if4_sweep(
         } else {
             uint32_t sb = e4m3_round(a / S6);
             sb = sb < 1u ? 1u : sb;
-            float w[16];
+            const int64_t col0 = (blk % blocks_per_row) * 16;
+            const int ctop = clamp_pattern((int)sb + hi);
+            // estimates of every (pattern, type) in the method's order
+            float b[16];
+            float W = 16.0f;
             if constexpr (WMSE)
-                load_weights16(imp, (blk % blocks_per_row) * 16, w);
-            double best = 0.0;
+                block_roots<16>(imp, root, wsum, roots_in_lds, col0, b, W);
+            uint32_t cw[4] = {0u, 0u, 0u, 0u};
+            float e1 = __builtin_huge_valf(), e2 = __builtin_huge_valf();
             int cb = (int)sb, cprev = -1;
             for (int k = lo; k <= hi; ++k) {
                 const int c = clamp_pattern((int)sb + k);
                 if (c == cprev)
                     continue;
-                const float4 t = tab[c];
-                const double Ef = fp4_error16<WMSE>(v, w, t.x, t.y);
-                if (cprev < 0 || Ef < best) { // the first candidate is always taken
-                    best = Ef;
-                    cb = c;
-                }
-                const double Ei = int4_error16<WMSE>(v, w, t.z, t.w);
-                if (Ei < best) {
-                    best = Ei;
-                    cb = c | 0x80;
-                }
                 cprev = c;
+                const float4 t = tab[c];
+                const float2 t2 = tab2[c];
+                float Ff, unused;
+                fp4_err32<WMSE, false>(v, b, t.y, Ff, unused, cw);
+                keep_best(Ff * t2.x, c, e1, e2, cb);
+                keep_best(int4_est16<WMSE>(v, b, t.w) * t2.y, c | 0x80, e1, e2, cb);
+            }
+            const float A = __builtin_fmaxf(a * invS * (1.0f + 4.0f * u),
+                                            6.0f * e4m3_value((uint32_t)ctop)) * (1.0f + 4.0f * u);
+            const float t1 = est_bound(e1, A, W, 40.0f * u), t2 = est_bound(e2, A, W, 40.0f * u);
+            const float4 tt = tab[ctop];
+            const bool finite = 6.0f * tt.x < __builtin_huge_valf() && 7.0f * tt.z < __builtin_huge_valf();
+            const bool certain = finite && e1 < __builtin_huge_valf() &&
+                                 (e2 == __builtin_huge_valf() || e2 - t2 > e1 + t1);
+            if (!certain) { // exact binary64 search
+                float w[16];
+                if constexpr (WMSE)
+                    load_weights16(imp, col0, w);
+                double best = 0.0;
+                cb = (int)sb;
+                cprev = -1;
+                for (int k = lo; k <= hi; ++k) {
+                    const int c = clamp_pattern((int)sb + k);
+                    if (c == cprev)
+                        continue;
+                    const float4 t = tab[c];
+                    const double Ef = fp4_error16<WMSE>(v, w, t.x, t.y);
+                    if (cprev < 0 || Ef < best) { // the first candidate is always taken
+                        best = Ef;
+                        cb = c;
+                    }
+                    const double Ei = int4_error16<WMSE>(v, w, t.z, t.w);
+                    if (Ei < best) {
+                        best = Ei;
+                        cb = c | 0x80;
+                    }
+                    cprev = c;
+                }
             }
             const float4 t = tab[cb & 0x7F];
             packed = (cb & 0x80) ? encode16_int4(v, t.w) : fp4_encode16(v, t.y);
@@ -1180,8 +1416,6 @@ static int resident_groups(K kernel)
 template <typename K>
 static int sweep_grid(K kernel, int64_t nb)
 {
-    static thread_local int cache_dev = -1;
-    (void)cache_dev;
     const int64_t need = (nb + kThreads - 1) / kThreads;
     const int cap = resident_groups(kernel);
     return (int)(need < cap ? (need < 1 ? 1 : need) : cap);
@@ -1197,12 +1431,16 @@ static void launch_nvfp4(const QuantArgs& a, int64_t nb, const float* part, int 
         hipLaunchKernelGGL((nvfp4_absmax<BF16, ROT>), grid, kThreads, 0, a.stream,
                            a.x, nb, part, npart, Sp, codes, a.scales);
     } else if (a.rule == kFourSix) {
-        if (a.objective == kWMSE)
-            hipLaunchKernelGGL((nvfp4_foursix<BF16, ROT, true>), grid, kThreads, 0, a.stream,
+        // one round of resident workgroups: each builds its LDS tables once
+        if (a.objective == kWMSE) {
+            auto k = nvfp4_foursix<BF16, ROT, true>;
+            hipLaunchKernelGGL(k, sweep_grid(k, nb), kThreads, 0, a.stream,
                                a.x, nb, bpr, a.importance, part, npart, Sp, codes, a.scales);
-        else
-            hipLaunchKernelGGL((nvfp4_foursix<BF16, ROT, false>), grid, kThreads, 0, a.stream,
+        } else {
+            auto k = nvfp4_foursix<BF16, ROT, false>;
+            hipLaunchKernelGGL(k, sweep_grid(k, nb), kThreads, 0, a.stream,
                                a.x, nb, bpr, a.importance, part, npart, Sp, codes, a.scales);
+        }
     } else {
         // the pages' two windows get a fully unrolled specialization
         const int win = (a.lo == -3 && a.hi == 7) ? 1 : ((a.lo == -8 && a.hi == 7) ? 2 : 0);
@@ -1231,15 +1469,20 @@ static void launch_if4(const QuantArgs& a, int64_t nb, const float* part, int np
     float* Sp = a.global_scale;
     uint2* codes = reinterpret_cast<uint2*>(a.codes);
     const bool wm = a.objective == kWMSE;
+    // kernels that build LDS tables run one round of resident workgroups
     if (a.rule == kSweep) {
-        if (wm)
-            hipLaunchKernelGGL((if4_sweep<BF16, ROT, true>), grid, kThreads, 0, a.stream, a.x, nb,
+        if (wm) {
+            auto k = if4_sweep<BF16, ROT, true>;
+            hipLaunchKernelGGL(k, sweep_grid(k, nb), kThreads, 0, a.stream, a.x, nb,
                                bpr, a.importance, part, npart, Sp, a.lo, a.hi, codes, a.scales);
-        else
-            hipLaunchKernelGGL((if4_sweep<BF16, ROT, false>), grid, kThreads, 0, a.stream, a.x, nb,
+        } else {
+            auto k = if4_sweep<BF16, ROT, false>;
+            hipLaunchKernelGGL(k, sweep_grid(k, nb), kThreads, 0, a.stream, a.x, nb,
                                bpr, a.importance, part, npart, Sp, a.lo, a.hi, codes, a.scales);
+        }
     } else if (wm) {
-        hipLaunchKernelGGL((if4_quant<BF16, ROT, true>), grid, kThreads, 0, a.stream,
+        auto k = if4_quant<BF16, ROT, true>;
+        hipLaunchKernelGGL(k, sweep_grid(k, nb), kThreads, 0, a.stream,
                            a.x, nb, bpr, a.importance, part, npart, Sp, codes, a.scales);
     } else {
         hipLaunchKernelGGL((if4_quant<BF16, ROT, false>), grid, kThreads, 0, a.stream,
@@ -1253,12 +1496,14 @@ static void launch_mxfp4(const QuantArgs& a, int64_t nb, int grid)
     uint4* codes = reinterpret_cast<uint4*>(a.codes);
     if (a.rule == kSweep) {
         const int64_t bpr = a.cols / 32;
-        if (a.objective == kWMSE)
-            hipLaunchKernelGGL((mxfp4_sweep<BF16, ROT, true>), grid, kThreads, 0, a.stream, a.x, nb,
+        if (a.objective == kWMSE) { // builds LDS tables: one round of resident workgroups
+            auto k = mxfp4_sweep<BF16, ROT, true>;
+            hipLaunchKernelGGL(k, sweep_grid(k, nb), kThreads, 0, a.stream, a.x, nb,
                                bpr, a.importance, a.lo, a.hi, codes, a.scales);
-        else
+        } else {
             hipLaunchKernelGGL((mxfp4_sweep<BF16, ROT, false>), grid, kThreads, 0, a.stream, a.x, nb,
                                bpr, a.importance, a.lo, a.hi, codes, a.scales);
+        }
     } else {
         hipLaunchKernelGGL((mxfp4_quant<BF16, ROT>), grid, kThreads, 0, a.stream, a.x, nb, codes, a.scales);
     }
