@@ -13,8 +13,10 @@ call; `roofline` is the dominant kernel (the sweep quantizer) timed alone
 with HIP events on the stream it runs on, against the 8 TB/s HBM peak;
 `cpu_baseline` is the CPU oracle on a bounded row sample of the same
 workload, and `parity_sample` compares the GPU's bytes on those rows with the
-oracle's.  `extensions` times Four Over Six, the MXFP4 exponent window, the
-IF4 pattern window and the FOCUS deploy encode.  `secondary` holds the 2 GiB
+oracle's.  `configs` times the other workloads with their own rules (c1
+NVFP4 AbsMax and ScaleSweep MSE, c3 MXFP4 with and without a 32-point
+Hadamard, c4 IF4); `extensions` times Four Over Six, the MXFP4 exponent
+window, the IF4 pattern window and the FOCUS deploy encode.  `secondary` holds the 2 GiB
 KV-cache workload (NVFP4 ScaleSweep MSE
 [-3, 7] with a fused 16-point Hadamard; quantize and dequantize timed
 separately).  A plain 1 GiB device copy is the achievable-bandwidth yardstick.
@@ -35,6 +37,8 @@ METRIC = "quantized Gelem/s + achieved HBM GB/s (% of peak), NVFP4 ScaleSweep MS
 
 
 COUNTERS = os.path.join(ROOT, "profiles", "nvfp4_sweep_wmse_hbm_counters.md")
+VALU_COUNTERS = os.path.join(ROOT, "profiles", "nvfp4_sweep_valu_counters.md")
+PEAK_VALU_LANE_OPS = 256 * 64 * 2.4e9          # non-packed lane-ops/s (fp32 and fp64 alike)
 KERNEL_SOURCES = ["block_scaled_fp4_fp4q_amd/csrc/fp4q_kernels.hip",
                   "block_scaled_fp4_fp4q_amd/csrc/fp4q_device.h"]
 
@@ -62,6 +66,25 @@ def measured_traffic():
     if not h or not t or h.group(1) != kernel_source_hash():
         return None
     return int(t.group(1))
+
+
+def measured_valu():
+    """Executed VALU lane-ops per element and VALU-busy fraction of the sweep
+    kernel from the committed rocprofv3 SQ counter summary, or None when the
+    kernel sources changed since."""
+    import re
+    try:
+        text = open(VALU_COUNTERS).read()
+    except OSError:
+        return None
+    h = re.search(r"Kernel sources sha256\[:16\] = `([0-9a-f]+)`", text)
+    ops = re.search(r"lane_ops_per_elem nvfp4_sweep_wmse_bf16_14336x4096 = ([0-9.]+)", text)
+    busy = re.search(r"valu_busy nvfp4_sweep_wmse_bf16_14336x4096 = ([0-9.]+)", text)
+    if not h or not ops or not busy or h.group(1) != kernel_source_hash():
+        return None
+    return {"lane_ops_per_elem": float(ops.group(1)), "valu_busy": float(busy.group(1)),
+            "peak_lane_ops_per_s": PEAK_VALU_LANE_OPS,
+            "source": "profiles/nvfp4_sweep_valu_counters.md (SQ_INSTS_VALU, GRBM_GUI_ACTIVE)"}
 
 
 def log(*a):
@@ -106,14 +129,15 @@ def event_time(fn, steps, warmup):
 
 
 def extensions(args, B, synth, dev, x2, imp, ws):
-    """The rules beyond ScaleSweep, each timed as one quantize call (global
-    scale computed) on its workload, with its MSE next to its baseline rule."""
+    """The other workloads (c1, c3, c4) and the rules beyond ScaleSweep, each
+    timed as one quantize call (global scale computed) on its workload, with
+    its error next to a baseline rule's.  Returns (configs, extensions)."""
     import torch
     steps = max(5, args.steps // 5)
     out = {}
 
     def run(name, workload, x, spec, importance=None, base_spec=None, err_imp=None, rotate=0,
-            bytes_per_elem=None):
+            bytes_per_elem=None, base_rotate=None):
         rows, cols = x.shape
         n = rows * cols
         codes = torch.empty(n // 2, dtype=torch.uint8, device=dev)
@@ -127,8 +151,12 @@ def extensions(args, B, synth, dev, x2, imp, ws):
         del xc
         espec = B.make_spec(spec.format, rotate=rotate)
         e = B.fp4q_error(espec, x, err_imp, codes, scales, gs, ws)
-        B.fp4q_quantize(base_spec, x, importance, codes, scales, gs, ws)
-        eb = B.fp4q_error(espec, x, err_imp, codes, scales, gs, ws)
+        base_rot = rotate if base_rotate is None else base_rotate
+        bcodes = torch.empty(n // 2, dtype=torch.uint8, device=dev)
+        bscales = torch.empty(n // base_spec.block, dtype=torch.uint8, device=dev)
+        B.fp4q_quantize(base_spec, x, importance, bcodes, bscales, gs, ws)
+        eb = B.fp4q_error(B.make_spec(base_spec.format, rotate=base_rot), x, err_imp, bcodes, bscales,
+                          gs, ws)
         k = 1 if err_imp is not None else 0
         gbps = n * bytes_per_elem / (ms * 1e-3) / 1e9
         out[name] = {"workload": workload, "quantize_ms": ms,
@@ -137,16 +165,38 @@ def extensions(args, B, synth, dev, x2, imp, ws):
                      "error": e[k], "baseline_error": eb[k],
                      "error_kind": "wmse" if k else "mse"}
         log(f"{name}: {ms:.3f} ms, {gbps:.0f} GB/s, err {e[k]:.6g} vs baseline {eb[k]:.6g}")
-        del codes, scales
+        del codes, scales, bcodes, bscales
 
     nv = 2 * 2.0 + 0.5 + 1.0 / 16          # global max read + read + codes + scales
     mx = 2.0 + 0.5 + 1.0 / 32
+
+    # ---- the other configurations with their own rules
+    x1 = to_dev(synth.c1(), dev)
+    f1 = 2 * 4.0 + 0.5 + 1.0 / 16
+    run("c1_nvfp4_absmax", "NVFP4 AbsMax, fp32 256x1024 N(0,1) with 1% x20 (cache-resident: "
+        "latency-bound, no roofline claim)", x1, B.make_spec(), base_spec=B.make_spec(),
+        bytes_per_elem=f1)
+    run("c1_nvfp4_sweep_mse", "NVFP4 ScaleSweep MSE [-3,7], fp32 256x1024 (cache-resident); "
+        "baseline AbsMax", x1, B.make_spec(B.FP4Q_NVFP4, B.FP4Q_SCALE_SWEEP, window=(-3, 7)),
+        base_spec=B.make_spec(), bytes_per_elem=f1)
+    del x1
+    x3 = to_dev(synth.c3(), dev)
+    run("c3_mxfp4_rtn", "MXFP4 OCP scale + RTN, bf16 activations 8192x4096, 8 outlier channels x50",
+        x3, B.make_spec(B.FP4Q_MXFP4), base_spec=B.make_spec(B.FP4Q_MXFP4), bytes_per_elem=mx)
+    run("c3_mxfp4_rtn_hadamard32", "MXFP4 with 32-point block Hadamard + RTN, same tensor; "
+        "baseline without rotation", x3, B.make_spec(B.FP4Q_MXFP4, rotate=32),
+        base_spec=B.make_spec(B.FP4Q_MXFP4), rotate=32, base_rotate=0, bytes_per_elem=mx)
+    x4 = to_dev(synth.c4()[0], dev)
+    run("c4_if4", "IF4 (FP4 or INT4 per block, indicator in the scale's sign bit), bf16 "
+        "8192x8192, half uniform / half spiky-Laplace blocks; baseline NVFP4 AbsMax",
+        x4, B.make_spec(B.FP4Q_IF4), base_spec=B.make_spec(), bytes_per_elem=nv)
+    configs = dict(out)
+    out.clear()
     run("nvfp4_four_over_six_wmse_c2",
         "NVFP4 Four Over Six (max onto 6 or 4), WMSE, bf16 weight 14336x4096; baseline AbsMax",
         x2, B.make_spec(B.FP4Q_NVFP4, B.FP4Q_SCALE_FOUR_OVER_SIX, B.FP4Q_OBJ_WMSE),
         importance=imp, base_spec=B.make_spec(), err_imp=imp, bytes_per_elem=nv)
 
-    x3 = to_dev(synth.c3(), dev)
     for rot in (0, 32):
         run(f"mxfp4_exponent_window_rot{rot}_c3",
             f"MXFP4 E8M0 exponent window [0,1], MSE, rotation {rot}, bf16 activations "
@@ -170,7 +220,6 @@ def extensions(args, B, synth, dev, x2, imp, ws):
     log(f"mxfp4 focus g8: {ms:.3f} ms, {gb:.0f} GB/s")
     del x3, c, r3, s3
 
-    x4 = to_dev(synth.c4()[0], dev)
     run("if4_pattern_window_c4",
         "IF4 (FP4 or INT4 per block) over E4M3 patterns [-3,7], MSE, bf16 8192x8192 "
         "half uniform / half spiky-Laplace blocks; baseline plain IF4",
@@ -178,7 +227,7 @@ def extensions(args, B, synth, dev, x2, imp, ws):
         base_spec=B.make_spec(B.FP4Q_IF4), bytes_per_elem=nv)
     del x4
     torch.cuda.empty_cache()
-    return out
+    return configs, out
 
 
 def main():
@@ -289,6 +338,8 @@ def main():
             "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
             "kernel_ms": ms_k,
             "algorithmic_bytes_per_launch": n * bytes_per_elem_kernel,
+            # the competing roof: the exact sweep is VALU-bound (see the VALU counters)
+            "valu": measured_valu(),
         },
     }
 
@@ -328,7 +379,7 @@ def main():
 
     # ---------------- extensions: 4/6, MXFP4 exponent window, IF4 window, FOCUS ----------------
     if not args.no_secondary:
-        result["extensions"] = extensions(args, B, synth, dev, xs[0], imp, ws)
+        result["configs"], result["extensions"] = extensions(args, B, synth, dev, xs[0], imp, ws)
 
     # ---------------- secondary: KV cache, sweep MSE + fused Hadamard ----------------
     if not args.no_secondary:

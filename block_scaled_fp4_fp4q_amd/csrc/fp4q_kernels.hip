@@ -188,14 +188,15 @@ __device__ __forceinline__ double int4_error16(const float* v, const float* w, f
 
 __device__ __forceinline__ uint2 encode16_int4(const float* v, float ri)
 {
+    // RNE is odd-symmetric, so clamping rint(v ri) to [-7, 7] gives
+    // sign(v) min(RNE(|v| ri), 7); its low four bits are the two's complement
+    // nibble (a signed zero gives 0)
     uint32_t lo = 0, hi = 0;
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-        const float q = __builtin_fminf(__builtin_rintf(__builtin_fabsf(v[i]) * ri), 7.0f);
-        int qi = (int)q;
-        if (__float_as_uint(v[i]) >> 31)
-            qi = -qi;
-        const uint32_t nib = (uint32_t)qi & 0xFu;
+        const float t = __builtin_rintf(v[i] * ri);
+        const int q = (int)__builtin_fmaxf(__builtin_fminf(t, 7.0f), -7.0f);
+        const uint32_t nib = (uint32_t)q & 0xFu;
         if (i < 8)
             lo |= nib << (4 * i);
         else
@@ -934,8 +935,41 @@ __global__ __launch_bounds__(kThreads) void mxfp4_sweep(
             }
             const float A = __builtin_fmaxf(a * rl, 6.0f * pow2f(K - 1)) * (1.0f + 4.0f * u);
             const float t1 = est_bound(e1, A, W, 32.0f * u), t2 = est_bound(e2, A, W, 32.0f * u);
-            if (e1 < __builtin_huge_valf() && (K == 1 || e2 - t2 > e1 + t1))
+            if (e1 < __builtin_huge_valf() && (K == 1 || e2 - t2 > e1 + t1)) {
                 eb = el + jb;
+            } else if (K == 2) {
+                // Two exponents whose reconstructions agree element by element
+                // (both exact multiples of 2^el) have equal binary64 errors, and
+                // the first wins: a block of one dominant element over values
+                // that round to zero either way.
+                bool same = true;
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    uint32_t c1 = cw[g], c2 = cw[g];
+                    float q1[8], q2[8];
+                    c1 = fp4_pack2_scaled<0>(c1, y[8 * g + 0], y[8 * g + 1], 1.0f);
+                    c1 = fp4_pack2_scaled<1>(c1, y[8 * g + 2], y[8 * g + 3], 1.0f);
+                    c1 = fp4_pack2_scaled<2>(c1, y[8 * g + 4], y[8 * g + 5], 1.0f);
+                    c1 = fp4_pack2_scaled<3>(c1, y[8 * g + 6], y[8 * g + 7], 1.0f);
+                    c2 = fp4_pack2_scaled<0>(c2, y[8 * g + 0], y[8 * g + 1], 2.0f);
+                    c2 = fp4_pack2_scaled<1>(c2, y[8 * g + 2], y[8 * g + 3], 2.0f);
+                    c2 = fp4_pack2_scaled<2>(c2, y[8 * g + 4], y[8 * g + 5], 2.0f);
+                    c2 = fp4_pack2_scaled<3>(c2, y[8 * g + 6], y[8 * g + 7], 2.0f);
+                    fp4_unpack2_scaled<0>(c1, q1[0], q1[1], 1.0f);
+                    fp4_unpack2_scaled<1>(c1, q1[2], q1[3], 1.0f);
+                    fp4_unpack2_scaled<2>(c1, q1[4], q1[5], 1.0f);
+                    fp4_unpack2_scaled<3>(c1, q1[6], q1[7], 1.0f);
+                    fp4_unpack2_scaled<0>(c2, q2[0], q2[1], 2.0f);
+                    fp4_unpack2_scaled<1>(c2, q2[2], q2[3], 2.0f);
+                    fp4_unpack2_scaled<2>(c2, q2[4], q2[5], 2.0f);
+                    fp4_unpack2_scaled<3>(c2, q2[6], q2[7], 2.0f);
+#pragma unroll
+                    for (int j = 0; j < 8; ++j)
+                        same = same && q1[j] == q2[j];
+                }
+                if (same)
+                    eb = el;
+            }
         }
         if (eb == 1000) { // exact binary64 search over the clamped window
             float w[32];
