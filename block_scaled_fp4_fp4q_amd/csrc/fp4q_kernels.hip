@@ -478,7 +478,7 @@ __device__ __forceinline__ void sweep_fixed(const float* v, const float* b, cons
     }
 }
 
-constexpr int kQueueCap = 1024; // fallback queue entries per workgroup (LDS)
+constexpr int kQueueHalf = 512; // fallback queue entries per workgroup and parity (LDS)
 
 template <bool BF16, bool ROT, bool WMSE, int WIN>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) void nvfp4_sweep(
@@ -491,8 +491,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
     // serves both), else 0.  Estimates are kept in units of S^2: s*s is
     // normal for every pattern, while D*D would underflow for small S.
     __shared__ float4 tab[128];
-    __shared__ int64_t queue[kQueueCap];
-    __shared__ uint32_t qn;
+    // uncertified blocks: iterations of even and odd index append to their
+    // own half, so a half's count is stable while it is checked
+    __shared__ int64_t queue[2][kQueueHalf];
+    __shared__ uint32_t qn[2];
     // sqrt(importance) per column and the importance sum per block column
     __shared__ float root[WMSE ? kRootCols : 1];
     __shared__ float wsum[WMSE ? kRootCols / 16 : 1];
@@ -507,8 +509,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
     bool roots_in_lds = false;
     if constexpr (WMSE)
         roots_in_lds = roots_prologue(imp, blocks_per_row * 16, root, wsum);
-    if (threadIdx.x == 0)
-        qn = 0;
+    if (threadIdx.x < 2)
+        qn[threadIdx.x] = 0;
     __syncthreads();
     // every pair (c, c+8) with c in [8, 0x76] an exact doubling (true unless S
     // pushes the steps to the ends of the binary32 range)
@@ -529,13 +531,13 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
     // lanes share a block, each evaluates every sixteenth offset of the
     // window, and the group keeps the least (error, pattern) pair -- the same
     // choice as a scan in ascending order that keeps the first least error.
-    auto drain = [&]() {
-        const uint32_t n = qn;
+    auto drain = [&](int h) {
+        const uint32_t n = qn[h];
         const int grp = threadIdx.x >> 4, sub = threadIdx.x & 15;
         for (uint32_t j0 = 0; j0 < n; j0 += kThreads / 16) {
             const uint32_t j = j0 + grp;
             const bool active = j < n;
-            const int64_t blk = queue[active ? j : 0];
+            const int64_t blk = queue[h][active ? j : 0];
             float v[16];
             load_block<16, BF16, false>(x, blk, v);
             if constexpr (ROT)
@@ -573,13 +575,14 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
         }
         __syncthreads();
         if (threadIdx.x == 0)
-            qn = 0;
+            qn[h] = 0;
         __syncthreads();
     };
 
     // every thread runs the same number of iterations, so the barriers below
     // are reached uniformly
-    for (int64_t base = (int64_t)blockIdx.x * kThreads; base < nblocks; base += stride) {
+    int h = 0; // queue half of this iteration
+    for (int64_t base = (int64_t)blockIdx.x * kThreads; base < nblocks; base += stride, h ^= 1) {
         const int64_t blk = base + threadIdx.x;
         if (blk < nblocks) {
             float v[16];
@@ -673,8 +676,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
                 }
             }
             if (queued) {
-                const uint32_t slot = atomicAdd(&qn, 1u); // < kQueueCap, see below
-                queue[slot] = blk;
+                const uint32_t slot = atomicAdd(&qn[h], 1u); // < kQueueHalf, see below
+                queue[h][slot] = blk;
             }
         }
         if constexpr (WMSE) {
@@ -682,12 +685,15 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
             col = col >= blocks_per_row ? col - blocks_per_row : col;
         }
         __syncthreads();
-        // at most kThreads entries join per iteration: drain before overflow
-        if (qn > (uint32_t)(kQueueCap - kThreads))
-            drain();
+        // qn[h] cannot change before every thread has passed the next
+        // iteration's barrier, so all threads read the same count here.  At
+        // most kThreads entries join a half per use: drain it before overflow.
+        if (qn[h] > (uint32_t)(kQueueHalf - kThreads))
+            drain(h);
     }
     __syncthreads();
-    drain();
+    drain(0);
+    drain(1);
 }
 
 // ---------------------------------------------------------------------------
