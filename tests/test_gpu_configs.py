@@ -237,3 +237,25 @@ def test_relaxed_full(B, ref, c2data, fmt, group):
         assert gs.item() == np.float32(want["S"])
     assert np.array_equal(scales.cpu().numpy(), want["scales"])
     assert np.array_equal(codes.cpu().numpy(), want["codes"])
+
+
+def test_sweep_queue_drains(B, ref):
+    # a constant tensor: patterns 0x78 and 0x7C both reconstruct 1.0 exactly, so
+    # every block is an exact tie that only the binary64 path may decide; at
+    # 2^20 blocks every workgroup fills and drains its fallback queue several
+    # times in mid-loop, with half the rows random so both paths interleave
+    rows, cols = 4096, 4096
+    x = np.ones((rows, cols), np.float32)
+    rng = np.random.default_rng(21)
+    # random rows within [-1, 1], so that S stays 1/1536 and the ties stay ties
+    x[1::2] = np.clip(rng.standard_normal((rows // 2, cols)) * 0.25, -1, 1).astype(np.float32)
+    imp = rng.lognormal(0, 1, cols).astype(np.float32)
+    xd, impd = to_dev(x), to_dev(imp)
+    for obj, window in ((1, (-8, 7)), (0, (-3, 7))):
+        codes, scales, gs = B.quantize(xd, scale_rule=1, objective=obj, window=window,
+                                       importance=impd if obj else None)
+        want = ref.quantize(x, rule=ref.SWEEP, objective=obj, window=window,
+                            importance=imp if obj else None, nthreads=THREADS)
+        assert gs.item() == np.float32(want["S"])
+        assert np.array_equal(scales.cpu().numpy(), want["scales"])
+        assert np.array_equal(codes.cpu().numpy(), want["codes"])
