@@ -496,7 +496,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
     __shared__ int64_t queue[2][kQueueHalf];
     __shared__ uint32_t qn[2];
     // sqrt(importance) per column and the importance sum per block column
-    __shared__ float root[WMSE ? kRootCols : 1];
+    __shared__ __attribute__((aligned(16))) float root[WMSE ? kRootCols : 1]; // read as float4
     __shared__ float wsum[WMSE ? kRootCols / 16 : 1];
     const float S = global_scale(partials, npart, Sp);
     for (int c = threadIdx.x; c < 128; c += kThreads) {
@@ -706,7 +706,7 @@ __global__ __launch_bounds__(kThreads) void if4_quant(
     const float* __restrict__ imp, const float* __restrict__ partials, int npart,
     float* __restrict__ Sp, uint2* __restrict__ codes, uint8_t* __restrict__ scales)
 {
-    __shared__ float root[WMSE ? kRootCols : 1];
+    __shared__ __attribute__((aligned(16))) float root[WMSE ? kRootCols : 1]; // read as float4
     __shared__ float wsum[WMSE ? kRootCols / 16 : 1];
     const float S = global_scale(partials, npart, Sp);
     bool roots_in_lds = false;
@@ -898,7 +898,7 @@ __global__ __launch_bounds__(kThreads) void mxfp4_sweep(
     const float* __restrict__ imp, int lo, int hi, uint4* __restrict__ codes,
     uint8_t* __restrict__ scales)
 {
-    __shared__ float root[WMSE ? kRootCols : 1];
+    __shared__ __attribute__((aligned(16))) float root[WMSE ? kRootCols : 1]; // read as float4
     __shared__ float wsum[WMSE ? kRootCols / 16 : 1];
     bool roots_in_lds = false;
     if constexpr (WMSE)
@@ -1012,7 +1012,7 @@ __global__ __launch_bounds__(kThreads) void nvfp4_foursix(
     const float* __restrict__ imp, const float* __restrict__ partials, int npart,
     float* __restrict__ Sp, uint2* __restrict__ codes, uint8_t* __restrict__ scales)
 {
-    __shared__ float root[WMSE ? kRootCols : 1];
+    __shared__ __attribute__((aligned(16))) float root[WMSE ? kRootCols : 1]; // read as float4
     __shared__ float wsum[WMSE ? kRootCols / 16 : 1];
     const float S = global_scale(partials, npart, Sp);
     bool roots_in_lds = false;
@@ -1089,7 +1089,7 @@ __global__ __launch_bounds__(kThreads) void if4_sweep(
 {
     __shared__ float4 tab[128];  // D, r, D_int = fl32(D 6/7), r_int
     __shared__ float2 tab2[128]; // s^2 and (s 6/7)^2: the estimates' units over S^2
-    __shared__ float root[WMSE ? kRootCols : 1];
+    __shared__ __attribute__((aligned(16))) float root[WMSE ? kRootCols : 1]; // read as float4
     __shared__ float wsum[WMSE ? kRootCols / 16 : 1];
     const float S = global_scale(partials, npart, Sp);
     for (int c = threadIdx.x; c < 128; c += kThreads) {

@@ -2,8 +2,10 @@
 Four Over Six (NVFP4), the E8M0 exponent window (MXFP4), the IF4 pattern
 window, and the FOCUS deploy-side encode with given coefficients.
 
-Each kernel decides in binary64 over the same binary32 encodes as the oracle,
-so codes, scale bytes, indicators and the global scale must be bit-exact.
+Each kernel's choice equals the binary64 comparison of the oracle's binary32
+encodes (from certified estimates, or the exact fallback where those do not
+separate), so codes, scale bytes, indicators and the global scale must be
+bit-exact.
 Sizes span several workgroups and end on a ragged tail; edge blocks cover
 zeros, signed zeros, subnormal and clamped scales, and saturation."""
 import numpy as np
@@ -241,3 +243,18 @@ def test_relaxed_edges_and_empty(B, ref):
     codes, scales, S = B.quantize_relaxed(e, c, 8)
     torch.cuda.synchronize()
     assert codes.numel() == 0 and S.item() == 1.0
+
+
+def test_wide_importance_vector(B, ref):
+    # more columns than the kernels keep square roots of in LDS (4096): the
+    # per-block square-root path of every weighted kernel
+    cols = 4096 + 512
+    x = student(7, cols, seed=95, dtype="bf16")
+    imp = weights(cols, 96)
+    compare(B, ref, x, B.FP4Q_NVFP4, B.FP4Q_SCALE_SWEEP, 1, window=(-8, 7), imp=imp)
+    compare(B, ref, x, B.FP4Q_NVFP4, B.FP4Q_SCALE_SWEEP, 1, window=(-3, 7), rotate=16, imp=imp)
+    compare(B, ref, x, B.FP4Q_NVFP4, B.FP4Q_SCALE_FOUR_OVER_SIX, 1, imp=imp)
+    compare(B, ref, x, B.FP4Q_IF4, B.FP4Q_SCALE_ABSMAX, 1, imp=imp)
+    compare(B, ref, x, B.FP4Q_IF4, B.FP4Q_SCALE_SWEEP, 1, window=(-3, 7), imp=imp)
+    compare(B, ref, x, B.FP4Q_MXFP4, B.FP4Q_SCALE_SWEEP, 1, window=(0, 1), imp=imp)
+    compare(B, ref, x, B.FP4Q_MXFP4, B.FP4Q_SCALE_SWEEP, 1, window=(-1, 2), rotate=32, imp=imp)
