@@ -582,11 +582,39 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
     // every thread runs the same number of iterations, so the barriers below
     // are reached uniformly
     int h = 0; // queue half of this iteration
+    // bf16 input of this lane's next block, loaded one iteration ahead so that
+    // its latency overlaps the current block's arithmetic (8 VGPRs; binary32
+    // input loads in place)
+    u32x4 pre[2];
+    if constexpr (BF16) {
+        const int64_t b0 = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+        if (b0 < nblocks) {
+            const u32x4* p = reinterpret_cast<const u32x4*>(x) + b0 * 2;
+            pre[0] = __builtin_nontemporal_load(p);
+            pre[1] = __builtin_nontemporal_load(p + 1);
+        }
+    }
     for (int64_t base = (int64_t)blockIdx.x * kThreads; base < nblocks; base += stride, h ^= 1) {
         const int64_t blk = base + threadIdx.x;
         if (blk < nblocks) {
             float v[16];
-            load_block<16, BF16>(x, blk, v);
+            if constexpr (BF16) {
+#pragma unroll
+                for (int q = 0; q < 2; ++q) {
+                    const u32x4 w = pre[q];
+                    v[8 * q + 0] = bf16_lo(w.x); v[8 * q + 1] = bf16_hi(w.x);
+                    v[8 * q + 2] = bf16_lo(w.y); v[8 * q + 3] = bf16_hi(w.y);
+                    v[8 * q + 4] = bf16_lo(w.z); v[8 * q + 5] = bf16_hi(w.z);
+                    v[8 * q + 6] = bf16_lo(w.w); v[8 * q + 7] = bf16_hi(w.w);
+                }
+                if (blk + stride < nblocks) {
+                    const u32x4* p = reinterpret_cast<const u32x4*>(x) + (blk + stride) * 2;
+                    pre[0] = __builtin_nontemporal_load(p);
+                    pre[1] = __builtin_nontemporal_load(p + 1);
+                }
+            } else {
+                load_block<16, BF16>(x, blk, v);
+            }
             if constexpr (ROT)
                 fwht<16>(v);
             const float a = block_absmax<16>(v);
