@@ -79,18 +79,6 @@ __device__ __forceinline__ float e2m1_q(float y)
     return __builtin_fminf(v, 6.0f);
 }
 
-// magnitude code 0..7 of an E2M1 value produced by e2m1_q
-__device__ __forceinline__ uint32_t e2m1_code(float v)
-{
-    return v < 2.0f ? (uint32_t)(v * 2.0f) : (v < 4.0f ? (uint32_t)v + 2u : (uint32_t)(v * 0.5f) + 4u);
-}
-
-__device__ __forceinline__ float e2m1_value(uint32_t m)
-{
-    const uint32_t e = (m >> 1) & 3u, f = m & 1u;
-    return e == 0 ? 0.5f * (float)f : __uint_as_float(((e + 126u) << 23) | (f << 22));
-}
-
 // ---- gfx950 FP4 conversion instructions ------------------------------------
 // v_cvt_scalef32_pk_fp4_f32 with a unit scale rounds two binary32 values to
 // the nearest E2M1 value (ties to the even code), saturates at +-6 and keeps

@@ -345,11 +345,13 @@ __global__ __launch_bounds__(kThreads) void nvfp4_absmax(
 // ---------------------------------------------------------------------------
 // NVFP4 ScaleSweep (MSE / WMSE)
 //
-// Fast path, per block: every candidate's error is estimated in binary32 in
-// units of its step D (y = |x| r with the method's own r = fl32(1/D), codes
-// from the hardware E2M1 conversion, which rounds exactly like the method, so
-// each code is the method's code; only the error arithmetic is shortened).
-// A rigorous bound T on |binary64 error - estimate| then certifies the pick:
+// Fast path, per block: every candidate's error is estimated in binary32 (y =
+// |x| r with the method's own r = fl32(1/D), codes from the hardware E2M1
+// conversion, which rounds exactly like the method, so each code is the
+// method's code; only the error arithmetic is shortened).  The sum is formed
+// in units of the candidate's step D and carried in units of S^2 (times the
+// pattern's exact s*s), which stays normal for any global scale.  A rigorous
+// bound T on |binary64 error / S^2 - estimate| then certifies the pick:
 // when the runner-up minus its bound exceeds the best plus its bound, the
 // binary64 argmin (ties to the smaller byte) is the estimated one.  Blocks
 // that are not certified -- exact ties, near ties, all-on-grid blocks -- go to
