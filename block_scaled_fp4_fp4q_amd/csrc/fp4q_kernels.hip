@@ -305,6 +305,35 @@ __device__ __forceinline__ float int4_est16(const float* v, const float* b, floa
     return F;
 }
 
+// the same estimate from signed values, also packing the method's INT4
+// nibbles: RNE is odd-symmetric, so q = clamp(rint(v ri), -7, 7) is
+// sign(v) min(RNE(|v| ri), 7), (v ri - q)^2 the same term, and the low four
+// bits of q its two's complement nibble
+template <bool WMSE>
+__device__ __forceinline__ float int4_est16_codes(const float* v, const float* b, float ri, uint2& words)
+{
+    float F = 0.0f;
+    uint32_t lo = 0, hi = 0;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        const float z = v[i] * ri;
+        const float q = __builtin_fmaxf(__builtin_fminf(__builtin_rintf(z), 7.0f), -7.0f);
+        float d;
+        if constexpr (WMSE)
+            d = __builtin_fmaf(-b[i], q, b[i] * z);
+        else
+            d = z - q;
+        F = __builtin_fmaf(d, d, F);
+        const uint32_t nib = (uint32_t)(int)q & 0xFu;
+        if (i < 8)
+            lo |= nib << (4 * i);
+        else
+            hi |= nib << (4 * (i - 8));
+    }
+    words = make_uint2(lo, hi);
+    return F;
+}
+
 // the 32 sign|magnitude nibbles of E2M1(v[i] * r) (hardware conversion)
 __device__ __forceinline__ uint4 fp4_encode32(const float* v, float r)
 {
@@ -772,10 +801,13 @@ __global__ __launch_bounds__(kThreads) void if4_quant(
             float W = 16.0f;
             if constexpr (WMSE)
                 block_roots<16>(imp, root, wsum, roots_in_lds, col0, b, W);
+            // the estimates also produce both candidates' codes: the FP4
+            // conversion words (of y = v r, as the encode) and the INT4 nibbles
             uint32_t cw[4] = {0u, 0u, 0u, 0u};
             float Ff, unused;
             fp4_err32<WMSE, false>(v, b, r, Ff, unused, cw);
-            const float Fi = int4_est16<WMSE>(v, b, ri);
+            uint2 int4_words;
+            const float Fi = int4_est16_codes<WMSE>(v, b, ri, int4_words);
             const float sz = sv * kInt4Step;
             const float Ef = Ff * (sv * sv), Ei = Fi * (sz * sz);
             const float A = __builtin_fmaxf(a * invS * (1.0f + 4.0f * u), 6.0f * sv) * (1.0f + 4.0f * u);
@@ -799,10 +831,10 @@ __global__ __launch_bounds__(kThreads) void if4_quant(
             }
             if (choice == 1) {
                 sbyte = sb | 0x80u;
-                packed = encode16_int4(v, ri);
+                packed = int4_words;
             } else {
                 sbyte = sb;
-                packed = fp4_encode16(v, r);
+                packed = make_uint2(cw[0], cw[1]);
             }
         }
         codes[blk] = packed;
@@ -1060,6 +1092,8 @@ __global__ __launch_bounds__(kThreads) void nvfp4_foursix(
         const float a = block_absmax<16>(v);
         uint32_t cb = 0;
         float r = 1.0f;
+        uint2 packed = make_uint2(0u, 0u);
+        bool have = false; // packed holds the chosen codes
         if (a != 0.0f) {
             uint32_t s6 = e4m3_round(a / S6), s4 = e4m3_round(a / S4);
             s6 = s6 < 1u ? 1u : s6;
@@ -1075,10 +1109,13 @@ __global__ __launch_bounds__(kThreads) void nvfp4_foursix(
                 float W = 16.0f;
                 if constexpr (WMSE)
                     block_roots<16>(imp, root, wsum, roots_in_lds, col0, b, W);
+                // the estimates' conversion words are each candidate's codes
                 uint32_t cw[4] = {0u, 0u, 0u, 0u};
                 float F6, F4, unused;
                 fp4_err32<WMSE, false>(v, b, r6, F6, unused, cw);
+                const uint2 codes6 = make_uint2(cw[0], cw[1]);
                 fp4_err32<WMSE, false>(v, b, r4, F4, unused, cw);
+                const uint2 codes4 = make_uint2(cw[0], cw[1]);
                 const float E6 = F6 * (v6 * v6), E4 = F4 * (v4 * v4);
                 const float A = __builtin_fmaxf(a * invS * (1.0f + 4.0f * u), 6.0f * __builtin_fmaxf(v6, v4)) *
                                 (1.0f + 4.0f * u);
@@ -1097,13 +1134,13 @@ __global__ __launch_bounds__(kThreads) void nvfp4_foursix(
                         load_weights16(imp, col0, w);
                     four = fp4_error16<WMSE>(v, w, D4, r4) < fp4_error16<WMSE>(v, w, D6, r6) ? 1 : 0;
                 }
-                if (four) {
+                if (four)
                     cb = s4;
-                    r = r4;
-                }
+                packed = four ? codes4 : codes6;
+                have = true;
             }
         }
-        codes[blk] = fp4_encode16(v, r);
+        codes[blk] = have ? packed : fp4_encode16(v, r);
         scales[blk] = (uint8_t)cb;
     }
 }
