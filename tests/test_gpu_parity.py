@@ -199,3 +199,47 @@ def test_deterministic(B):
     torch.cuda.synchronize()
     for u, v in zip(a, b):
         assert torch.equal(u, v)
+
+
+def test_graph_capture_replays(B, ref):
+    # quantize (partial maxima + sweep) and dequantize launch kernels only, so
+    # they can be captured; each replay, with eager work and synchronizations
+    # in between, must reproduce the eager results
+    x, imp = inputs("bf16", 64, 512, seed=77)
+    xd, impd = to_dev(x), to_dev(imp)
+    spec = B.make_spec(B.FP4Q_NVFP4, B.FP4Q_SCALE_SWEEP, B.FP4Q_OBJ_WMSE, (-8, 7))
+    dspec = B.make_spec(B.FP4Q_NVFP4)
+    ws = B.alloc_workspace(spec, *x.shape, DEV)
+    n = x.size
+
+    def outputs():
+        return (torch.empty(n // 2, dtype=torch.uint8, device=DEV),
+                torch.empty(n // 16, dtype=torch.uint8, device=DEV),
+                torch.empty(1, dtype=torch.float32, device=DEV),
+                torch.empty(x.shape, dtype=torch.bfloat16, device=DEV))
+
+    ce, se, ge, ye = outputs()
+    B.fp4q_quantize(spec, xd, impd, ce, se, ge, ws)
+    B.fp4q_dequantize(dspec, ce, se, ge, *x.shape, 0, ye)
+    torch.cuda.synchronize()
+
+    c, s, g, y = outputs()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):                   # warm-up outside the capture
+        B.fp4q_quantize(spec, xd, impd, c, s, g, ws)
+        B.fp4q_dequantize(dspec, c, s, g, *x.shape, 0, y)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        B.fp4q_quantize(spec, xd, impd, c, s, g, ws)
+        B.fp4q_dequantize(dspec, c, s, g, *x.shape, 0, y)
+    for _ in range(3):
+        for t in (c, s, g, y):
+            t.zero_()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(c, ce) and torch.equal(s, se) and torch.equal(g, ge)
+        assert torch.equal(y.view(torch.int16), ye.view(torch.int16))
