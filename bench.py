@@ -10,7 +10,14 @@ in the 256 MB Infinity Cache.
 
 Printed: one JSON line (rank 0).  `value` is quantized Gelem/s of the whole
 call; `roofline` is the dominant kernel (the sweep quantizer) timed alone
-with HIP events on the stream it runs on, against the 8 TB/s HBM peak;
+with HIP events on the stream it runs on.  That kernel is bound by its
+vector-ALU work, so the roofline is the VALU's: the exact estimate of all 16
+candidates needs 48 binary32 operations, 8 FP4 encodes and 8 FP4 decodes per
+element, the conversions weighted by their issue cost relative to an FMA
+(measured by block_scaled_fp4_fp4q_amd/valu_issue, a microbenchmark run as a
+child process), against the published 157.3 TFLOP/s binary32 vector peak
+(78.6 T FMA lane-ops/s); the 8 TB/s HBM roofline of the same kernel is
+reported beside it;
 `cpu_baseline` is the CPU oracle on a bounded row sample of the same
 workload, and `parity_sample` compares the GPU's bytes on those rows with the
 oracle's.  `configs` times the other workloads with their own rules (c1
@@ -24,6 +31,7 @@ separately).  A plain 1 GiB device copy is the achievable-bandwidth yardstick.
 import argparse
 import json
 import os
+import subprocess
 import sys
 import time
 
@@ -38,7 +46,15 @@ METRIC = "quantized Gelem/s + achieved HBM GB/s (% of peak), NVFP4 ScaleSweep MS
 
 COUNTERS = os.path.join(ROOT, "profiles", "nvfp4_sweep_wmse_hbm_counters.md")
 VALU_COUNTERS = os.path.join(ROOT, "profiles", "nvfp4_sweep_valu_counters.md")
-PEAK_VALU_LANE_OPS = 256 * 64 * 2.4e9          # non-packed lane-ops/s (fp32 and fp64 alike)
+VALU_ISSUE = os.path.join(ROOT, "block_scaled_fp4_fp4q_amd", "valu_issue")
+# published binary32 vector peak, 157.3 TFLOP/s, as FMA lane-ops/s: 256 CUs x
+# 4 SIMDs x 2.4 GHz x 32 lanes per cycle (a wave64 FMA issues in 2 cycles)
+PEAK_FP32_LANE_OPS = 157.3e12 / 2
+# per element of the sweep over 16 patterns in 8 exactly doubling pairs: per
+# pair, y = |x| r and b y (shared), two residual FMAs and two accumulating
+# FMAs (6 binary32 ops), one encode and one decode instruction (each converts
+# two elements of one candidate, two candidates per pair)
+SWEEP16_MIX = {"fp32": 48, "encode": 8, "decode": 8}
 KERNEL_SOURCES = ["block_scaled_fp4_fp4q_amd/csrc/fp4q_kernels.hip",
                   "block_scaled_fp4_fp4q_amd/csrc/fp4q_device.h"]
 
@@ -69,9 +85,10 @@ def measured_traffic():
 
 
 def measured_valu():
-    """Executed VALU lane-ops per element and VALU-busy fraction of the sweep
-    kernel from the committed rocprofv3 SQ counter summary, or None when the
-    kernel sources changed since."""
+    """Executed VALU lane-ops per element, AMD's VALUBusy and the fraction of
+    the VALU's measured issue capacity used by the sweep kernel, from the
+    committed rocprofv3 SQ counter summary, or None when the kernel sources
+    changed since."""
     import re
     try:
         text = open(VALU_COUNTERS).read()
@@ -80,11 +97,58 @@ def measured_valu():
     h = re.search(r"Kernel sources sha256\[:16\] = `([0-9a-f]+)`", text)
     ops = re.search(r"lane_ops_per_elem nvfp4_sweep_wmse_bf16_14336x4096 = ([0-9.]+)", text)
     busy = re.search(r"valu_busy nvfp4_sweep_wmse_bf16_14336x4096 = ([0-9.]+)", text)
-    if not h or not ops or not busy or h.group(1) != kernel_source_hash():
+    util = re.search(r"issue_capacity_used nvfp4_sweep_wmse_bf16_14336x4096 = ([0-9.]+)", text)
+    if not h or not ops or not busy or not util or h.group(1) != kernel_source_hash():
         return None
     return {"lane_ops_per_elem": float(ops.group(1)), "valu_busy": float(busy.group(1)),
-            "peak_lane_ops_per_s": PEAK_VALU_LANE_OPS,
-            "source": "profiles/nvfp4_sweep_valu_counters.md (SQ_INSTS_VALU, GRBM_GUI_ACTIVE)"}
+            "issue_capacity_used": float(util.group(1)),
+            "source": "profiles/nvfp4_sweep_valu_counters.md (SQ_INSTS_VALU, "
+                      "SQ_ACTIVE_INST_VALU, GRBM_GUI_ACTIVE)"}
+
+
+def valu_issue_costs():
+    """Issue cost of one wave64 instruction per class, in core-clock cycles of
+    one SIMD, measured by the valu_issue microbenchmark in a child process; None
+    when it is not built or fails."""
+    if not os.path.exists(VALU_ISSUE):
+        log(f"{VALU_ISSUE} is not built: no ALU roofline (run __graft_entry__.build())")
+        return None
+    try:
+        r = subprocess.run([VALU_ISSUE], capture_output=True, text=True, timeout=120, check=True)
+        return json.loads(r.stdout.strip().splitlines()[-1])
+    except (subprocess.SubprocessError, ValueError, IndexError) as e:
+        log(f"valu_issue failed: {e}")
+        return None
+
+
+def roofline(n, ms_k, kernel_gbps, bytes_per_elem, issue):
+    """The sweep kernel against the VALU roof (its binding resource), with the
+    HBM roof beside it; the HBM roof alone when the issue costs are missing."""
+    hbm = {"bound": "hbm", "achieved": kernel_gbps, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+           "frac": kernel_gbps / PEAK_HBM_GBPS,
+           "algorithmic_bytes_per_launch": n * bytes_per_elem}
+    common = {"kernel": "nvfp4_sweep<bf16, no rotation, wmse>", "kernel_ms": ms_k,
+              "traffic": measured_traffic(),
+              "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, "
+                              "copy-calibrated)",
+              "valu_counters": measured_valu()}
+    if issue is None:
+        return {**hbm, **common}
+    c = issue["cycles_per_wave64_instr"]
+    w_enc = c["v_cvt_scalef32_pk_fp4_f32"] / c["v_fma_f32"]
+    w_dec = c["v_cvt_scalef32_pk_f32_fp4"] / c["v_fma_f32"]
+    ops = SWEEP16_MIX["fp32"] + SWEEP16_MIX["encode"] * w_enc + SWEEP16_MIX["decode"] * w_dec
+    achieved = n * ops / (ms_k * 1e-3) / 1e12
+    peak = PEAK_FP32_LANE_OPS / 1e12
+    return {"bound": "alu", "achieved": achieved, "peak": peak,
+            "unit": "T VALU lane-ops/s (binary32 FMA equivalents)", "frac": achieved / peak,
+            **common,
+            "algorithmic_lane_ops_per_elem": ops,
+            "algorithmic_lane_ops_per_launch": n * ops,
+            "instruction_mix_per_elem": SWEEP16_MIX,
+            "conversion_weights": {"encode": w_enc, "decode": w_dec},
+            "issue_costs": issue,
+            "hbm": hbm}
 
 
 def log(*a):
@@ -101,6 +165,8 @@ def parse():
     p.add_argument("--no-secondary", action="store_true")
     p.add_argument("--no-cpu", action="store_true")
     p.add_argument("--cpu-rows", type=int, default=2048)
+    p.add_argument("--no-issue", action="store_true",
+                   help="skip the VALU issue-cost microbenchmark (the roofline falls back to HBM)")
     return p.parse_args()
 
 
@@ -239,6 +305,11 @@ def main():
               "scale; see DESIGN.md).  Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
 
+    # VALU issue costs first, in a child process, before this one opens the GPU
+    issue = None if args.no_issue else valu_issue_costs()
+    if issue is not None:
+        log("VALU issue cycles per wave64 instruction:", issue["cycles_per_wave64_instr"])
+
     import torch
     from block_scaled_fp4_fp4q_amd import binding as B
     from block_scaled_fp4_fp4q_amd import synth
@@ -328,20 +399,7 @@ def main():
         "nvfp4_sweep_wmse": wmse_sweep,
         "nvfp4_absmax_mse": mse_abs,
         "nvfp4_absmax_wmse": wmse_abs,
-        "roofline": {
-            "kernel": "nvfp4_sweep<bf16, no rotation, wmse>",
-            "bound": "hbm",
-            "achieved": kernel_gbps,
-            "peak": PEAK_HBM_GBPS,
-            "unit": "GB/s",
-            "frac": kernel_gbps / PEAK_HBM_GBPS,
-            "traffic": measured_traffic(),
-            "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
-            "kernel_ms": ms_k,
-            "algorithmic_bytes_per_launch": n * bytes_per_elem_kernel,
-            # the competing roof: the exact sweep is VALU-bound (see the VALU counters)
-            "valu": measured_valu(),
-        },
+        "roofline": roofline(n, ms_k, kernel_gbps, bytes_per_elem_kernel, issue),
     }
 
     # ---------------- CPU oracle on a row sample of the same workload ----------------
