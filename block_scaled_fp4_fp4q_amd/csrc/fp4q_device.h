@@ -195,6 +195,18 @@ __device__ __forceinline__ float block_absmax(const float* v)
     return a;
 }
 
+// ---- quad exchange (lanes 4k..4k+3) -------------------------------------------
+
+// the same register of lane (lane ^ X) within this lane's quad, X = 1 or 2
+// (DPP quad_perm [1,0,3,2] or [2,3,0,1]; every lane of the quad must be active)
+template <int X>
+__device__ __forceinline__ float quad_xor(float v)
+{
+    static_assert(X == 1 || X == 2, "quad exchange partner");
+    constexpr int ctrl = X == 1 ? 0xB1 : 0x4E;
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), ctrl, 0xF, 0xF, true));
+}
+
 // ---- wave reductions (64 lanes) -------------------------------------------------
 
 __device__ __forceinline__ float wave_max(float v)

@@ -854,6 +854,8 @@ __device__ __forceinline__ int floor_log2_f32(float a)
     return -149 + (31 - __clz((int)u)); // subnormal, u != 0
 }
 
+// one lane per block (binary32 input): block maximum, E8M0 exponent, the
+// hardware encode of |v| 2^-e
 template <bool BF16, bool ROT>
 __global__ __launch_bounds__(kThreads) void mxfp4_quant(
     const void* __restrict__ x, int64_t nblocks, uint4* __restrict__ codes,
@@ -873,6 +875,73 @@ __global__ __launch_bounds__(kThreads) void mxfp4_quant(
         const float r = __uint_as_float((uint32_t)(127 - e) << 23);
         codes[blk] = fp4_encode32(v, r);
         scales[blk] = (uint8_t)(e + 127);
+    }
+}
+
+// MXFP4 quantize of bf16 input with four lanes per block: lane s of a quad holds
+// elements 8s..8s+7, so every load instruction reads 1 KiB contiguous (one
+// 16-byte piece per lane) instead of 16-byte pieces 64 bytes apart.  The block
+// maximum and the Hadamard's two widest stages cross the quad through DPP;
+// each lane writes its four code bytes.
+template <bool ROT>
+__global__ __launch_bounds__(kThreads) void mxfp4_quant_quad(
+    const void* __restrict__ x, int64_t nblocks, uint32_t* __restrict__ codes,
+    uint8_t* __restrict__ scales)
+{
+    const int s = threadIdx.x & 3;
+    const u32x4* xp = reinterpret_cast<const u32x4*>(x);
+    // a quad's lanes are consecutive and nblocks * 4 is a multiple of 4, so a
+    // quad is active or inactive as a whole (the DPP exchanges need that)
+    for (int64_t q = (int64_t)blockIdx.x * kThreads + threadIdx.x; q < nblocks * 4;
+         q += (int64_t)gridDim.x * kThreads) {
+        const u32x4 w = __builtin_nontemporal_load(xp + q);
+        float v[8];
+        v[0] = bf16_lo(w.x); v[1] = bf16_hi(w.x);
+        v[2] = bf16_lo(w.y); v[3] = bf16_hi(w.y);
+        v[4] = bf16_lo(w.z); v[5] = bf16_hi(w.z);
+        v[6] = bf16_lo(w.w); v[7] = bf16_hi(w.w);
+        if constexpr (ROT) {
+            // butterfly widths 1, 2, 4 inside the lane, then 8 and 16 across
+            // the quad: the in-register transform's order and roundings.  Across
+            // lanes the lower partner keeps a + b and the upper a - b, both as
+            // one rounding of fma(+-1, own, partner's).
+#pragma unroll
+            for (int h = 1; h < 8; h *= 2)
+#pragma unroll
+                for (int i = 0; i < 8; i += 2 * h)
+#pragma unroll
+                    for (int j = i; j < i + h; ++j) {
+                        const float a = v[j], b = v[j + h];
+                        v[j] = a + b;
+                        v[j + h] = a - b;
+                    }
+            const float sg1 = (s & 1) ? -1.0f : 1.0f, sg2 = (s & 2) ? -1.0f : 1.0f;
+#pragma unroll
+            for (int k = 0; k < 8; ++k)
+                v[k] = __builtin_fmaf(sg1, v[k], quad_xor<1>(v[k]));
+#pragma unroll
+            for (int k = 0; k < 8; ++k)
+                v[k] = __builtin_fmaf(sg2, v[k], quad_xor<2>(v[k]));
+            const float c = __uint_as_float(0x3E3504F3u); // fl32(1/sqrt(32))
+#pragma unroll
+            for (int k = 0; k < 8; ++k)
+                v[k] = v[k] * c;
+        }
+        float a = block_absmax<8>(v);
+        a = __builtin_fmaxf(a, quad_xor<1>(a));
+        a = __builtin_fmaxf(a, quad_xor<2>(a));
+        int e = (a == 0.0f) ? -127 : floor_log2_f32(a) - 2;
+        e = e < -127 ? -127 : (e > 127 ? 127 : e);
+        const float r = __uint_as_float((uint32_t)(127 - e) << 23);
+        // every byte of the word is written: start from any value
+        uint32_t c = __builtin_nondeterministic_value(0u);
+        c = fp4_pack2<0>(c, v[0] * r, v[1] * r);
+        c = fp4_pack2<1>(c, v[2] * r, v[3] * r);
+        c = fp4_pack2<2>(c, v[4] * r, v[5] * r);
+        c = fp4_pack2<3>(c, v[6] * r, v[7] * r);
+        codes[q] = c; // codes holds nblocks * 4 words
+        if (s == 0)
+            scales[q >> 2] = (uint8_t)(e + 127);
     }
 }
 
@@ -1612,7 +1681,12 @@ static void launch_mxfp4(const QuantArgs& a, int64_t nb, int grid)
                                bpr, a.importance, a.lo, a.hi, codes, a.scales);
         }
     } else {
-        hipLaunchKernelGGL((mxfp4_quant<BF16, ROT>), grid, kThreads, 0, a.stream, a.x, nb, codes, a.scales);
+        if constexpr (BF16) // four lanes per block
+            hipLaunchKernelGGL((mxfp4_quant_quad<ROT>), grid_for(nb * 4, kQuantGroupCap), kThreads, 0,
+                               a.stream, a.x, nb, reinterpret_cast<uint32_t*>(a.codes), a.scales);
+        else
+            hipLaunchKernelGGL((mxfp4_quant<BF16, ROT>), grid, kThreads, 0, a.stream, a.x, nb, codes,
+                               a.scales);
     }
 }
 
