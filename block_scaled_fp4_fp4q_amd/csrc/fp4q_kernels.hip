@@ -1386,6 +1386,75 @@ __global__ __launch_bounds__(kThreads) void relaxed_quant(
     }
 }
 
+// The same encode for bf16 input with L = B/8 lanes per block (four for
+// MXFP4, two for NVFP4): lane s holds elements 8s..8s+7 from one coalesced
+// 16-byte load, and the coefficient of its group; the block maximum crosses
+// the lanes through DPP, and each lane writes its four code bytes.
+template <int FMT, int GROUP, bool GIVEN>
+__global__ __launch_bounds__(kThreads) void relaxed_quant_lanes(
+    const void* __restrict__ x, int64_t nblocks, const float* __restrict__ coef,
+    const float* __restrict__ partials, int npart, float* __restrict__ Sp,
+    uint32_t* __restrict__ codes, uint8_t* __restrict__ scales)
+{
+    constexpr int B = (FMT == kMXFP4) ? 32 : 16;
+    constexpr int L = B / 8;
+    constexpr int NG = B / GROUP;
+    const int s = threadIdx.x & (L - 1);
+    const float S = (FMT == kMXFP4) ? 1.0f : global_scale(partials, npart, Sp);
+    const float S6 = 6.0f * S;
+    const u32x4* xp = reinterpret_cast<const u32x4*>(x);
+    // a block's lanes are consecutive and nblocks * L is a multiple of L, so
+    // they are active or inactive together (the DPP exchanges need that)
+    for (int64_t q = (int64_t)blockIdx.x * kThreads + threadIdx.x; q < nblocks * L;
+         q += (int64_t)gridDim.x * kThreads) {
+        const int64_t blk = q / L;
+        const u32x4 w = __builtin_nontemporal_load(xp + q);
+        float v[8];
+        v[0] = bf16_lo(w.x); v[1] = bf16_hi(w.x);
+        v[2] = bf16_lo(w.y); v[3] = bf16_hi(w.y);
+        v[4] = bf16_lo(w.z); v[5] = bf16_hi(w.z);
+        v[6] = bf16_lo(w.w); v[7] = bf16_hi(w.w);
+        uint32_t byte;
+        float D;
+        if constexpr (GIVEN) {
+            byte = scales[blk];
+            if constexpr (FMT == kMXFP4)
+                D = pow2f((int)byte - 127);
+            else
+                D = e4m3_value(byte) * S;
+        } else {
+            float a = block_absmax<8>(v);
+            a = __builtin_fmaxf(a, quad_xor<1>(a));
+            if constexpr (L == 4)
+                a = __builtin_fmaxf(a, quad_xor<2>(a));
+            if constexpr (FMT == kMXFP4) {
+                const int e = mx_exponent(a);
+                byte = (uint32_t)(e + 127);
+                D = pow2f(e);
+            } else {
+                byte = 0;
+                D = 0.0f;
+                if (a != 0.0f) {
+                    byte = e4m3_round(a / S6);
+                    byte = byte < 1u ? 1u : byte;
+                    D = e4m3_value(byte) * S;
+                }
+            }
+        }
+        const float cg = coef[blk * NG + (8 * s) / GROUP];
+        const float r = (D == 0.0f) ? 0.0f : 1.0f / (D * cg); // a zero step keeps signs only
+        uint32_t wv = 0;
+        wv = fp4_pack2<0>(wv, v[0] * r, v[1] * r);
+        wv = fp4_pack2<1>(wv, v[2] * r, v[3] * r);
+        wv = fp4_pack2<2>(wv, v[4] * r, v[5] * r);
+        wv = fp4_pack2<3>(wv, v[6] * r, v[7] * r);
+        codes[q] = wv; // codes holds nblocks * L words
+        if constexpr (!GIVEN)
+            if (s == 0)
+                scales[blk] = (uint8_t)byte;
+    }
+}
+
 // ---------------------------------------------------------------------------
 // dequantize and error
 // ---------------------------------------------------------------------------
@@ -1761,6 +1830,18 @@ hipError_t launch_quantize(const QuantArgs& a)
 template <int FMT, bool BF16, int GROUP>
 static void launch_relaxed_g(const RelaxArgs& a, int64_t nb, const float* part, int npart, int grid)
 {
+    if constexpr (BF16) { // B/8 lanes per block
+        constexpr int L = (FMT == kMXFP4) ? 4 : 2;
+        const int g = grid_for(nb * L, kQuantGroupCap);
+        uint32_t* codes = reinterpret_cast<uint32_t*>(a.codes);
+        if (a.scales_given)
+            hipLaunchKernelGGL((relaxed_quant_lanes<FMT, GROUP, true>), g, kThreads, 0, a.stream,
+                               a.x, nb, a.coef, part, npart, a.global_scale, codes, a.scales);
+        else
+            hipLaunchKernelGGL((relaxed_quant_lanes<FMT, GROUP, false>), g, kThreads, 0, a.stream,
+                               a.x, nb, a.coef, part, npart, a.global_scale, codes, a.scales);
+        return;
+    }
     if (a.scales_given)
         hipLaunchKernelGGL((relaxed_quant<FMT, BF16, GROUP, true>), grid, kThreads, 0, a.stream,
                            a.x, nb, a.coef, part, npart, a.global_scale, a.codes, a.scales);

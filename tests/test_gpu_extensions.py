@@ -235,9 +235,11 @@ def test_relaxed_edges_and_empty(B, ref):
     x[0, 16:32] = -0.0
     x[1] *= np.float32(2.0 ** -135)
     x[2, :8] = np.float32(6.0)
-    for f in (B.FP4Q_NVFP4, B.FP4Q_MXFP4):
-        for group in (8, 16 if f == B.FP4Q_NVFP4 else 32):
-            relaxed_case(B, ref, x, f, group, seed=91)
+    # binary32 input runs one lane per block, bf16 input B/8 lanes per block
+    for xin in (x, synth.f32_to_bf16_bits(x)):
+        for f in (B.FP4Q_NVFP4, B.FP4Q_MXFP4):
+            for group in (8, 16 if f == B.FP4Q_NVFP4 else 32):
+                relaxed_case(B, ref, xin, f, group, seed=91)
     e = torch.empty(0, 64, dtype=torch.float32, device=DEV)
     c = torch.empty(0, 8, dtype=torch.float32, device=DEV)
     codes, scales, S = B.quantize_relaxed(e, c, 8)
