@@ -878,6 +878,53 @@ __global__ __launch_bounds__(kThreads) void mxfp4_quant(
     }
 }
 
+// eight bf16 values of a 16-byte piece, widened
+__device__ __forceinline__ void unpack8_bf16(const u32x4 w, float* v)
+{
+    v[0] = bf16_lo(w.x); v[1] = bf16_hi(w.x);
+    v[2] = bf16_lo(w.y); v[3] = bf16_hi(w.y);
+    v[4] = bf16_lo(w.z); v[5] = bf16_hi(w.z);
+    v[6] = bf16_lo(w.w); v[7] = bf16_hi(w.w);
+}
+
+// 32-point Hadamard of a block spread over a quad (lane s holds elements
+// 8s..8s+7): butterfly widths 1, 2, 4 inside the lane, then 8 and 16 across
+// the quad -- the in-register transform's order and roundings.  Across lanes
+// the lower partner keeps a + b and the upper a - b, each as one rounding of
+// fma(+-1, own, partner's).
+__device__ __forceinline__ void fwht32_quad(float* v, int s)
+{
+#pragma unroll
+    for (int h = 1; h < 8; h *= 2)
+#pragma unroll
+        for (int i = 0; i < 8; i += 2 * h)
+#pragma unroll
+            for (int j = i; j < i + h; ++j) {
+                const float a = v[j], b = v[j + h];
+                v[j] = a + b;
+                v[j + h] = a - b;
+            }
+    const float sg1 = (s & 1) ? -1.0f : 1.0f, sg2 = (s & 2) ? -1.0f : 1.0f;
+#pragma unroll
+    for (int k = 0; k < 8; ++k)
+        v[k] = __builtin_fmaf(sg1, v[k], quad_xor<1>(v[k]));
+#pragma unroll
+    for (int k = 0; k < 8; ++k)
+        v[k] = __builtin_fmaf(sg2, v[k], quad_xor<2>(v[k]));
+    const float c = __uint_as_float(0x3E3504F3u); // fl32(1/sqrt(32))
+#pragma unroll
+    for (int k = 0; k < 8; ++k)
+        v[k] = v[k] * c;
+}
+
+// the block maximum of a quad's 32 values
+__device__ __forceinline__ float quad_absmax(const float* v)
+{
+    float a = block_absmax<8>(v);
+    a = __builtin_fmaxf(a, quad_xor<1>(a));
+    return __builtin_fmaxf(a, quad_xor<2>(a));
+}
+
 // MXFP4 quantize of bf16 input with four lanes per block: lane s of a quad holds
 // elements 8s..8s+7, so every load instruction reads 1 KiB contiguous (one
 // 16-byte piece per lane) instead of 16-byte pieces 64 bytes apart.  The block
@@ -894,42 +941,11 @@ __global__ __launch_bounds__(kThreads) void mxfp4_quant_quad(
     // quad is active or inactive as a whole (the DPP exchanges need that)
     for (int64_t q = (int64_t)blockIdx.x * kThreads + threadIdx.x; q < nblocks * 4;
          q += (int64_t)gridDim.x * kThreads) {
-        const u32x4 w = __builtin_nontemporal_load(xp + q);
         float v[8];
-        v[0] = bf16_lo(w.x); v[1] = bf16_hi(w.x);
-        v[2] = bf16_lo(w.y); v[3] = bf16_hi(w.y);
-        v[4] = bf16_lo(w.z); v[5] = bf16_hi(w.z);
-        v[6] = bf16_lo(w.w); v[7] = bf16_hi(w.w);
-        if constexpr (ROT) {
-            // butterfly widths 1, 2, 4 inside the lane, then 8 and 16 across
-            // the quad: the in-register transform's order and roundings.  Across
-            // lanes the lower partner keeps a + b and the upper a - b, both as
-            // one rounding of fma(+-1, own, partner's).
-#pragma unroll
-            for (int h = 1; h < 8; h *= 2)
-#pragma unroll
-                for (int i = 0; i < 8; i += 2 * h)
-#pragma unroll
-                    for (int j = i; j < i + h; ++j) {
-                        const float a = v[j], b = v[j + h];
-                        v[j] = a + b;
-                        v[j + h] = a - b;
-                    }
-            const float sg1 = (s & 1) ? -1.0f : 1.0f, sg2 = (s & 2) ? -1.0f : 1.0f;
-#pragma unroll
-            for (int k = 0; k < 8; ++k)
-                v[k] = __builtin_fmaf(sg1, v[k], quad_xor<1>(v[k]));
-#pragma unroll
-            for (int k = 0; k < 8; ++k)
-                v[k] = __builtin_fmaf(sg2, v[k], quad_xor<2>(v[k]));
-            const float c = __uint_as_float(0x3E3504F3u); // fl32(1/sqrt(32))
-#pragma unroll
-            for (int k = 0; k < 8; ++k)
-                v[k] = v[k] * c;
-        }
-        float a = block_absmax<8>(v);
-        a = __builtin_fmaxf(a, quad_xor<1>(a));
-        a = __builtin_fmaxf(a, quad_xor<2>(a));
+        unpack8_bf16(__builtin_nontemporal_load(xp + q), v);
+        if constexpr (ROT)
+            fwht32_quad(v, s);
+        const float a = quad_absmax(v);
         int e = (a == 0.0f) ? -127 : floor_log2_f32(a) - 2;
         e = e < -127 ? -127 : (e > 127 ? 127 : e);
         const float r = __uint_as_float((uint32_t)(127 - e) << 23);
@@ -1408,12 +1424,8 @@ __global__ __launch_bounds__(kThreads) void relaxed_quant_lanes(
     for (int64_t q = (int64_t)blockIdx.x * kThreads + threadIdx.x; q < nblocks * L;
          q += (int64_t)gridDim.x * kThreads) {
         const int64_t blk = q / L;
-        const u32x4 w = __builtin_nontemporal_load(xp + q);
         float v[8];
-        v[0] = bf16_lo(w.x); v[1] = bf16_hi(w.x);
-        v[2] = bf16_lo(w.y); v[3] = bf16_hi(w.y);
-        v[4] = bf16_lo(w.z); v[5] = bf16_hi(w.z);
-        v[6] = bf16_lo(w.w); v[7] = bf16_hi(w.w);
+        unpack8_bf16(__builtin_nontemporal_load(xp + q), v);
         uint32_t byte;
         float D;
         if constexpr (GIVEN) {

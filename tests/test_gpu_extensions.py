@@ -104,9 +104,11 @@ def test_mxfp4_wide_windows(B, ref, window):
     compare(B, ref, x, B.FP4Q_MXFP4, B.FP4Q_SCALE_SWEEP, 0, window=window)
 
 
-def test_mxfp4_window_extremes(B, ref):
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_mxfp4_window_extremes(B, ref, dtype):
     # exponents clamped at both ends of E8M0, subnormal inputs, zero blocks,
-    # signed zeros and values that saturate
+    # signed zeros and values that saturate (bf16 input runs four lanes per
+    # block, and the clamped windows its gathered exact search)
     rng = np.random.default_rng(53)
     x = rng.standard_normal((8, 128)).astype(np.float32)
     x[0] *= np.float32(2.0 ** -140)        # subnormal, OCP exponent below -127
@@ -117,6 +119,9 @@ def test_mxfp4_window_extremes(B, ref):
     x[3, 5] = -np.float32(3.4e38)
     x[4, :32] = np.float32(7.9)            # above 6 * 2^e: saturation at e, exact at e+1
     x[5, :32] = np.float32(2.0 ** -149)    # smallest subnormal
+    if dtype == "bf16":
+        x[3, 5] = -np.float32(3.38e38)     # -3.4e38 would round to -inf (inputs must be finite)
+        x = synth.f32_to_bf16_bits(x)
     for window in ((0, 1), (-126, 126), (-3, 3)):
         compare(B, ref, x, B.FP4Q_MXFP4, B.FP4Q_SCALE_SWEEP, 0, window=window)
 
