@@ -148,15 +148,19 @@ def test_edge_blocks(B, ref):
             run_case(B, ref, fmt, rule, 0, rot, x, None)
 
 
-def test_mxfp4_bf16_edge_blocks(B, ref):
-    # bf16 MXFP4 runs four lanes per block (DPP maximum and Hadamard stages):
-    # the adversarial blocks in bf16, and a tensor of one block
+def test_lane_split_bf16_edge_blocks(B, ref):
+    # bf16 MXFP4 runs four lanes per block and bf16 IF4 (MSE) two: the DPP
+    # maximum, Hadamard stages and ordered exact sums on the adversarial
+    # blocks in bf16, and on a tensor of one block
     from test_oracle_spec import adversarial_nvfp4
     x = synth.f32_to_bf16_bits(adversarial_nvfp4().reshape(-1, 64))
     x1 = synth.f32_to_bf16_bits(np.linspace(-3, 5, 32, dtype=np.float32).reshape(1, 32))
     for rot in (0, 32):
         run_case(B, ref, "mxfp4", 0, 0, rot, x, None)
         run_case(B, ref, "mxfp4", 0, 0, rot, x1, None)
+    for rot in (0, 16):
+        run_case(B, ref, "if4", 0, 0, rot, x, None)
+        run_case(B, ref, "if4", 0, 0, rot, x1[:, :16], None)
 
 
 def test_empty_and_single_block(B, ref):
