@@ -20,7 +20,8 @@ child process), against the published 157.3 TFLOP/s binary32 vector peak
 reported beside it;
 `cpu_baseline` is the CPU oracle on a bounded row sample of the same
 workload, and `parity_sample` compares the GPU's bytes on those rows with the
-oracle's.  `configs` times the other workloads with their own rules (c1
+oracle's; every other workload carries a `parity_sample` of its leading rows
+(about 2^18 elements) as well.  `configs` times the other workloads with their own rules (c1
 NVFP4 AbsMax and ScaleSweep MSE, c3 MXFP4 with and without a 32-point
 Hadamard, c4 IF4); `extensions` times Four Over Six, the MXFP4 exponent
 window, the IF4 pattern window and the FOCUS deploy encode.  `secondary` holds the 2 GiB
@@ -195,16 +196,52 @@ def event_time(fn, steps, warmup):
     return s.elapsed_time(e) / steps, wall
 
 
-def extensions(args, B, synth, dev, x2, imp, ws):
+SAMPLE_ELEMS = 1 << 18  # elements of the leading rows re-quantized by the oracle per workload
+
+
+def sample_parity(x_h, spec, codes, scales, gs, importance=None, relaxed=None):
+    """The oracle on the leading rows of a workload (about SAMPLE_ELEMS
+    elements), under the global scale the GPU computed for the whole tensor,
+    against the GPU's bytes for those rows: mismatch counts and the oracle's
+    near-tie blocks (second-best error within 1e-6 relative of the best)."""
+    from oracle import ref
+    rows, cols = x_h.shape
+    r = max(1, min(rows, SAMPLE_ELEMS // cols))
+    xs = np.ascontiguousarray(x_h[:r])
+    S = None if spec.format == 1 else float(gs.item())  # MXFP4 has no global scale
+    cores = len(os.sched_getaffinity(0))
+    if relaxed is not None:
+        coef, group = relaxed
+        want = ref.quantize_relaxed(xs, np.ascontiguousarray(coef[:r]), group, fmt=spec.format,
+                                    global_scale=S, nthreads=cores)
+    else:
+        want = ref.quantize(xs, fmt=spec.format, rule=spec.scale_rule, objective=spec.objective,
+                            window=(spec.sweep_lo, spec.sweep_hi), rotate=spec.rotate,
+                            global_scale=S, importance=importance, nthreads=cores, errors=True)
+    nb = r * cols // spec.block
+    got_s = scales.cpu().numpy()[:nb]
+    got_c = codes.cpu().numpy()[: r * cols // 2]
+    out = {"rows": r, "blocks": nb, "scale_mismatches": int(np.sum(got_s != want["scales"])),
+           "code_bytes_mismatched": int(np.sum(got_c != want["codes"]))}
+    if "best" in want:
+        live = want["best"] > 0
+        gap = np.where(live, (want["second"] - want["best"]) / np.where(live, want["best"], 1),
+                       np.inf)
+        out["oracle_near_tie_blocks"] = int(np.sum(gap < 1e-6))
+    return out
+
+
+def extensions(args, B, synth, dev, x2, imp, ws, x2_h, imp_h):
     """The other workloads (c1, c3, c4) and the rules beyond ScaleSweep, each
     timed as one quantize call (global scale computed) on its workload, with
-    its error next to a baseline rule's.  Returns (configs, extensions)."""
+    its error next to a baseline rule's and, unless --no-cpu, the oracle's
+    bytes on a row sample.  Returns (configs, extensions)."""
     import torch
     steps = max(5, args.steps // 5)
     out = {}
 
     def run(name, workload, x, spec, importance=None, base_spec=None, err_imp=None, rotate=0,
-            bytes_per_elem=None, base_rotate=None):
+            bytes_per_elem=None, base_rotate=None, x_h=None, imp_host=None):
         rows, cols = x.shape
         n = rows * cols
         codes = torch.empty(n // 2, dtype=torch.uint8, device=dev)
@@ -216,6 +253,10 @@ def extensions(args, B, synth, dev, x2, imp, ws):
         ms, _ = event_time(lambda i: B.fp4q_quantize(spec, xc[i % ncopy], importance, codes, scales,
                                                      gs, ws), steps, 2)
         del xc
+        # the oracle on a row sample, before the baseline below overwrites gs
+        ps = None
+        if x_h is not None and not args.no_cpu:
+            ps = sample_parity(x_h, spec, codes, scales, gs, importance=imp_host)
         espec = B.make_spec(spec.format, rotate=rotate)
         e = B.fp4q_error(espec, x, err_imp, codes, scales, gs, ws)
         base_rot = rotate if base_rotate is None else base_rotate
@@ -231,47 +272,57 @@ def extensions(args, B, synth, dev, x2, imp, ws):
                      "quantize_frac_of_peak": gbps / PEAK_HBM_GBPS,
                      "error": e[k], "baseline_error": eb[k],
                      "error_kind": "wmse" if k else "mse"}
-        log(f"{name}: {ms:.3f} ms, {gbps:.0f} GB/s, err {e[k]:.6g} vs baseline {eb[k]:.6g}")
+        if ps is not None:
+            out[name]["parity_sample"] = ps
+        log(f"{name}: {ms:.3f} ms, {gbps:.0f} GB/s, err {e[k]:.6g} vs baseline {eb[k]:.6g}"
+            + (f", parity {out[name]['parity_sample']}" if "parity_sample" in out[name] else ""))
         del codes, scales, bcodes, bscales
 
     nv = 2 * 2.0 + 0.5 + 1.0 / 16          # global max read + read + codes + scales
     mx = 2.0 + 0.5 + 1.0 / 32
 
     # ---- the other configurations with their own rules
-    x1 = to_dev(synth.c1(), dev)
+    x1_h = synth.c1()
+    x1 = to_dev(x1_h, dev)
     f1 = 2 * 4.0 + 0.5 + 1.0 / 16
     run("c1_nvfp4_absmax", "NVFP4 AbsMax, fp32 256x1024 N(0,1) with 1% x20 (cache-resident: "
         "latency-bound, no roofline claim)", x1, B.make_spec(), base_spec=B.make_spec(),
-        bytes_per_elem=f1)
+        bytes_per_elem=f1, x_h=x1_h)
     run("c1_nvfp4_sweep_mse", "NVFP4 ScaleSweep MSE [-3,7], fp32 256x1024 (cache-resident); "
         "baseline AbsMax", x1, B.make_spec(B.FP4Q_NVFP4, B.FP4Q_SCALE_SWEEP, window=(-3, 7)),
-        base_spec=B.make_spec(), bytes_per_elem=f1)
+        base_spec=B.make_spec(), bytes_per_elem=f1, x_h=x1_h)
     del x1
-    x3 = to_dev(synth.c3(), dev)
+    x3_h = synth.c3()
+    x3 = to_dev(x3_h, dev)
     run("c3_mxfp4_rtn", "MXFP4 OCP scale + RTN, bf16 activations 8192x4096, 8 outlier channels x50",
-        x3, B.make_spec(B.FP4Q_MXFP4), base_spec=B.make_spec(B.FP4Q_MXFP4), bytes_per_elem=mx)
+        x3, B.make_spec(B.FP4Q_MXFP4), base_spec=B.make_spec(B.FP4Q_MXFP4), bytes_per_elem=mx,
+        x_h=x3_h)
     run("c3_mxfp4_rtn_hadamard32", "MXFP4 with 32-point block Hadamard + RTN, same tensor; "
         "baseline without rotation", x3, B.make_spec(B.FP4Q_MXFP4, rotate=32),
-        base_spec=B.make_spec(B.FP4Q_MXFP4), rotate=32, base_rotate=0, bytes_per_elem=mx)
-    x4 = to_dev(synth.c4()[0], dev)
+        base_spec=B.make_spec(B.FP4Q_MXFP4), rotate=32, base_rotate=0, bytes_per_elem=mx,
+        x_h=x3_h)
+    x4_h = synth.c4()[0]
+    x4 = to_dev(x4_h, dev)
     run("c4_if4", "IF4 (FP4 or INT4 per block, indicator in the scale's sign bit), bf16 "
         "8192x8192, half uniform / half spiky-Laplace blocks; baseline NVFP4 AbsMax",
-        x4, B.make_spec(B.FP4Q_IF4), base_spec=B.make_spec(), bytes_per_elem=nv)
+        x4, B.make_spec(B.FP4Q_IF4), base_spec=B.make_spec(), bytes_per_elem=nv, x_h=x4_h)
     configs = dict(out)
     out.clear()
     run("nvfp4_four_over_six_wmse_c2",
         "NVFP4 Four Over Six (max onto 6 or 4), WMSE, bf16 weight 14336x4096; baseline AbsMax",
         x2, B.make_spec(B.FP4Q_NVFP4, B.FP4Q_SCALE_FOUR_OVER_SIX, B.FP4Q_OBJ_WMSE),
-        importance=imp, base_spec=B.make_spec(), err_imp=imp, bytes_per_elem=nv)
+        importance=imp, base_spec=B.make_spec(), err_imp=imp, bytes_per_elem=nv, x_h=x2_h,
+        imp_host=imp_h)
 
     for rot in (0, 32):
         run(f"mxfp4_exponent_window_rot{rot}_c3",
             f"MXFP4 E8M0 exponent window [0,1], MSE, rotation {rot}, bf16 activations "
             "8192x4096 with 8 outlier channels; baseline the OCP exponent",
             x3, B.make_spec(B.FP4Q_MXFP4, B.FP4Q_SCALE_SWEEP, window=(0, 1), rotate=rot),
-            base_spec=B.make_spec(B.FP4Q_MXFP4, rotate=rot), rotate=rot, bytes_per_elem=mx)
-    c = torch.from_numpy(np.random.default_rng(12).lognormal(0.0, 0.08, (8192, 4096 // 8))
-                         .astype(np.float32)).to(dev)
+            base_spec=B.make_spec(B.FP4Q_MXFP4, rotate=rot), rotate=rot, bytes_per_elem=mx,
+            x_h=x3_h)
+    c_h = np.random.default_rng(12).lognormal(0.0, 0.08, (8192, 4096 // 8)).astype(np.float32)
+    c = torch.from_numpy(c_h).to(dev)
     r3 = torch.empty(8192 * 4096 // 2, dtype=torch.uint8, device=dev)
     s3 = torch.empty(8192 * 4096 // 32, dtype=torch.uint8, device=dev)
     spec_r = B.make_spec(B.FP4Q_MXFP4)
@@ -284,14 +335,19 @@ def extensions(args, B, synth, dev, x2, imp, ws):
         "workload": "FOCUS deploy encode, MXFP4, one coefficient per 8 elements "
                     "(lognormal(0,0.08)), bf16 8192x4096", "quantize_ms": ms,
         "quantize_gbps": gb, "quantize_frac_of_peak": gb / PEAK_HBM_GBPS}
-    log(f"mxfp4 focus g8: {ms:.3f} ms, {gb:.0f} GB/s")
+    if not args.no_cpu:
+        B.fp4q_quantize_relaxed(spec_r, x3, c, 8, False, r3, s3, None, ws)
+        out["mxfp4_focus_deploy_g8_c3"]["parity_sample"] = sample_parity(
+            x3_h, spec_r, r3, s3, None, relaxed=(c_h, 8))
+    log(f"mxfp4 focus g8: {ms:.3f} ms, {gb:.0f} GB/s, "
+        f"parity {out['mxfp4_focus_deploy_g8_c3'].get('parity_sample')}")
     del x3, c, r3, s3
 
     run("if4_pattern_window_c4",
         "IF4 (FP4 or INT4 per block) over E4M3 patterns [-3,7], MSE, bf16 8192x8192 "
         "half uniform / half spiky-Laplace blocks; baseline plain IF4",
         x4, B.make_spec(B.FP4Q_IF4, B.FP4Q_SCALE_SWEEP, window=(-3, 7)),
-        base_spec=B.make_spec(B.FP4Q_IF4), bytes_per_elem=nv)
+        base_spec=B.make_spec(B.FP4Q_IF4), bytes_per_elem=nv, x_h=x4_h)
     del x4
     torch.cuda.empty_cache()
     return configs, out
@@ -438,7 +494,8 @@ def main():
 
     # ---------------- extensions: 4/6, MXFP4 exponent window, IF4 window, FOCUS ----------------
     if not args.no_secondary:
-        result["configs"], result["extensions"] = extensions(args, B, synth, dev, xs[0], imp, ws)
+        result["configs"], result["extensions"] = extensions(args, B, synth, dev, xs[0], imp, ws,
+                                                             x_h, imp_h)
 
     # ---------------- secondary: KV cache, sweep MSE + fused Hadamard ----------------
     if not args.no_secondary:
@@ -448,6 +505,7 @@ def main():
         kv_h = synth.c5()
         log(f"generated c5 {kv_h.shape} in {time.time() - t:.1f}s")
         kv = to_dev(kv_h, dev)
+        kv_head = np.ascontiguousarray(kv_h[: SAMPLE_ELEMS // kv_h.shape[1]])
         del kv_h
         kr, kc = kv.shape
         kn = kr * kc
@@ -483,7 +541,12 @@ def main():
                 "nvfp4_absmax_mse": kmse_abs,
             },
         }
-        log(f"c5 quantize {kms:.3f} ms, sweep kernel {kms_k:.3f} ms, dequant {dms:.3f} ms")
+        if not args.no_cpu:
+            # kc_, ks_, kg_ hold the last quantize of kv (S given: the S of the full call)
+            result["secondary"]["kv_cache_sweep_mse_hadamard16"]["parity_sample"] = sample_parity(
+                kv_head, kspec, kc_, ks_, kg_)
+        log(f"c5 quantize {kms:.3f} ms, sweep kernel {kms_k:.3f} ms, dequant {dms:.3f} ms, parity "
+            f"{result['secondary']['kv_cache_sweep_mse_hadamard16'].get('parity_sample')}")
 
     print(json.dumps(result), flush=True)
 
