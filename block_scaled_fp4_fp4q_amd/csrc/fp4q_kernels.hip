@@ -205,6 +205,28 @@ __device__ __forceinline__ uint2 encode16_int4(const float* v, float ri)
     return make_uint2(lo, hi);
 }
 
+// fp4_error16 and int4_error16 (MSE) of one block together, element by
+// element from a per-lane LDS copy of the block (loop not unrolled): the same
+// terms and order of summation with a few live registers, for the rare blocks
+// whose estimates do not decide -- so that this path does not set the
+// register budget, and with it the occupancy, of the common path
+__device__ __forceinline__ void if4_exact_errors_lds(const float* slot, float D, float r, float Di,
+                                                     float ri, double& ef, double& ei)
+{
+    ef = 0.0;
+    ei = 0.0;
+#pragma unroll 1
+    for (int i = 0; i < 16; ++i) {
+        const float a = __builtin_fabsf(slot[i]);
+        const float xf = e2m1_q(a * r) * D;
+        const double df = (double)a - (double)xf;
+        const float xi = __builtin_fminf(__builtin_rintf(a * ri), 7.0f) * Di;
+        const double di = (double)a - (double)xi;
+        ef = ef + df * df;
+        ei = ei + di * di;
+    }
+}
+
 __device__ __forceinline__ void load_weights16(const float* __restrict__ imp, int64_t col0, float* w)
 {
     const float4* p = reinterpret_cast<const float4*>(imp + col0);
@@ -767,6 +789,12 @@ __global__ __launch_bounds__(kThreads) void if4_quant(
 {
     __shared__ __attribute__((aligned(16))) float root[WMSE ? kRootCols : 1]; // read as float4
     __shared__ float wsum[WMSE ? kRootCols / 16 : 1];
+    // MSE: each lane's current block for the exact path (a stride of 20 floats
+    // keeps the 16-byte stores of eight consecutive lanes on distinct banks).
+    // With weights the roots table already bounds the workgroups per CU, so
+    // the block stays in registers there.
+    __shared__ __attribute__((aligned(16))) float xslot[WMSE ? 4 : kThreads * 20];
+    float* slot = xslot + (WMSE ? 0 : threadIdx.x * 20);
     const float S = global_scale(partials, npart, Sp);
     bool roots_in_lds = false;
     if constexpr (WMSE)
@@ -781,6 +809,13 @@ __global__ __launch_bounds__(kThreads) void if4_quant(
         if constexpr (ROT)
             fwht<16>(v);
         const float a = block_absmax<16>(v);
+        if constexpr (!WMSE) {
+            // stored now so that v is dead after the estimates (the register
+            // budget of the common path), read back only by the exact path
+#pragma unroll
+            for (int i = 0; i < 16; i += 4)
+                *reinterpret_cast<float4*>(slot + i) = make_float4(v[i], v[i + 1], v[i + 2], v[i + 3]);
+        }
         uint2 packed;
         uint32_t sbyte;
         if (a == 0.0f) {
@@ -821,12 +856,16 @@ __global__ __launch_bounds__(kThreads) void if4_quant(
                 else if (Ef + Tf <= Ei - Ti)
                     choice = 0;
             }
-            if (choice < 0) { // exact binary64 comparison
-                float w[16];
-                if constexpr (WMSE)
+            if (choice < 0) { // exact binary64 comparison (rare)
+                double ef, ei;
+                if constexpr (WMSE) {
+                    float w[16];
                     load_weights16(imp, col0, w);
-                const double ef = fp4_error16<WMSE>(v, w, D, r);
-                const double ei = int4_error16<WMSE>(v, w, Di, ri);
+                    ef = fp4_error16<true>(v, w, D, r);
+                    ei = int4_error16<true>(v, w, Di, ri);
+                } else {
+                    if4_exact_errors_lds(slot, D, r, Di, ri, ef, ei);
+                }
                 choice = ei < ef ? 1 : 0;
             }
             if (choice == 1) {
