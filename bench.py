@@ -160,8 +160,9 @@ def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=50)
-    p.add_argument("--warmup", type=int, default=50,
-                   help="untimed steps first (the clock settles over the first ~10 ms of load)")
+    p.add_argument("--warmup", type=int, default=200,
+                   help="untimed steps first (the core clock settles over ~20-30 ms of load, "
+                        "about 150 steps)")
     p.add_argument("--copies", type=int, default=4, help="input copies cycled per step")
     p.add_argument("--no-secondary", action="store_true")
     p.add_argument("--no-cpu", action="store_true")
