@@ -165,7 +165,8 @@ def parse():
                         "about 150 steps)")
     p.add_argument("--copies", type=int, default=4, help="input copies cycled per step")
     p.add_argument("--no-secondary", action="store_true")
-    p.add_argument("--no-cpu", action="store_true")
+    p.add_argument("--no-cpu", action="store_true",
+                   help="skip the CPU oracle leg: the baseline timing and every parity sample")
     p.add_argument("--cpu-rows", type=int, default=2048)
     p.add_argument("--no-issue", action="store_true",
                    help="skip the VALU issue-cost microbenchmark (the roofline falls back to HBM)")
