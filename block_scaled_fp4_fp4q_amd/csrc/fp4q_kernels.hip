@@ -4,16 +4,19 @@
 // Data flow of one quantize call (NVFP4 / IF4 with a computed global scale):
 //   amax_*      one read of x (rotated on the fly when asked) -> one partial
 //               maximum per workgroup in the workspace;
-//   finalize    one workgroup reduces the partials to G and writes
-//               S = max(G/1536, 2^-117) (1 for G == 0) to the caller's
-//               global_scale (ScaleSweep page, Method 2: S = max|x|/(256*6));
-//   *_quant     one lane per block: load + widen, optional Hadamard, block
-//               max, base scale, candidate search, encode, packed store.
-// MXFP4 and a caller-supplied S skip the first two kernels.
+//   *_quant,    every workgroup reduces the partials to G, S = max(G/1536,
+//   *_sweep     2^-117) (1 for G == 0; ScaleSweep page, Method 2: S =
+//               max|x|/(256*6)), and workgroup 0 publishes S; then per block:
+//               load + widen, optional Hadamard, block max, base scale,
+//               candidate search, encode, packed store.  Most kernels give a
+//               block to one lane; the streaming bf16 MXFP4 ones give it to
+//               four (lanes per block, below).
+// MXFP4 and a caller-supplied S skip the first kernel.
 //
-// Block decisions are exact: candidate errors are accumulated in binary64
-// over the same binary32 encode sequence the method defines, and ties keep
-// the smaller scale byte (the FP4 branch for IF4).
+// Block decisions equal the method's binary64 argmin (ties keep the smaller
+// scale byte, the FP4 branch for IF4): candidates are compared by binary32
+// estimates over the method's own codes, certified by a rigorous error bound,
+// and blocks the bound leaves undecided take the exact binary64 evaluation.
 #include "fp4q_device.h"
 #include "fp4q_launch.h"
 
@@ -95,7 +98,9 @@ __global__ __launch_bounds__(kThreads) void amax_rot(const void* __restrict__ x,
 }
 
 // G = max of the partials; S = G / 1536, floored at 2^-117 (so every
-// D = s*S is a normal binary32 with a finite reciprocal), 1 when G == 0
+// D = s*S is a normal binary32 with a finite reciprocal), 1 when G == 0.
+// Launched for an empty tensor only (n == 0 partials: S = 1), where no
+// quantize kernel runs to publish S.
 __global__ __launch_bounds__(1024) void finalize_scale(const float* __restrict__ partials, int n,
                                                        float* __restrict__ S_out)
 {
