@@ -180,13 +180,35 @@ def to_dev(x, dev):
     return torch.from_numpy(x).to(dev)
 
 
-def event_time(fn, steps, warmup):
+SETTLE_MS = 30.0  # GPU time of untimed calls before a secondary timing (clock settling)
+
+
+def event_time(fn, steps, warmup, settle_ms=0.0):
     """Average ms per call of fn(i) over `steps` calls, HIP events on the
-    current stream (the stream every library call is issued on)."""
+    current stream (the stream every library call is issued on).  `warmup`
+    untimed calls come first; with settle_ms > 0, more untimed calls follow
+    until about that much GPU time has run, so that a short workload timed
+    after an idle stretch (input generation on the host) is not measured
+    while the core clock is still rising, and at least settle_ms / 3 of calls
+    are timed."""
     import torch
     for i in range(warmup):
         fn(i)
     torch.cuda.synchronize()
+    if settle_ms > 0.0:
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s.record()
+        for i in range(3):
+            fn(i)
+        e.record()
+        torch.cuda.synchronize()
+        per = max(s.elapsed_time(e) / 3, 1e-3)
+        for i in range(int(settle_ms / per) + 1):
+            fn(i)
+        torch.cuda.synchronize()
+        # and a timed region of at least a third of that, so that a short
+        # workload is not timed over a fraction of a millisecond
+        steps = max(steps, int(settle_ms / 3 / per) + 1)
     s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
     s.record()
@@ -253,7 +275,7 @@ def extensions(args, B, synth, dev, x2, imp, ws, x2_h, imp_h):
         ncopy = max(2, -(-(512 << 20) // (x.numel() * x.element_size())))
         xc = [x] + [x.clone() for _ in range(ncopy - 1)]
         ms, _ = event_time(lambda i: B.fp4q_quantize(spec, xc[i % ncopy], importance, codes, scales,
-                                                     gs, ws), steps, 2)
+                                                     gs, ws), steps, 2, SETTLE_MS)
         del xc
         # the oracle on a row sample, before the baseline below overwrites gs
         ps = None
@@ -330,7 +352,7 @@ def extensions(args, B, synth, dev, x2, imp, ws, x2_h, imp_h):
     spec_r = B.make_spec(B.FP4Q_MXFP4)
     x3c = [x3] + [x3.clone() for _ in range(7)]
     ms, _ = event_time(lambda i: B.fp4q_quantize_relaxed(spec_r, x3c[i % 8], c, 8, False, r3, s3,
-                                                         None, ws), steps, 2)
+                                                         None, ws), steps, 2, SETTLE_MS)
     del x3c
     gb = 8192 * 4096 * (mx + 4.0 / 8) / (ms * 1e-3) / 1e9
     out["mxfp4_focus_deploy_g8_c3"] = {
@@ -417,7 +439,7 @@ def main():
     # whose FETCH_SIZE / WRITE_SIZE calibrate the HBM traffic counters
     ref_src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
     ref_dst = torch.empty_like(ref_src)
-    cms, _ = event_time(lambda i: ref_dst.copy_(ref_src), 10, 2)
+    cms, _ = event_time(lambda i: ref_dst.copy_(ref_src), 10, 2, SETTLE_MS)
     copy_gbps = 2 * ref_src.numel() / (cms * 1e-3) / 1e9
     del ref_src, ref_dst
     log(f"device copy 1 GiB: {copy_gbps:.0f} GB/s")
@@ -518,10 +540,13 @@ def main():
                          torch.empty(kn // 16, dtype=torch.uint8, device=dev),
                          torch.empty(1, dtype=torch.float32, device=dev))
         ksteps = max(5, args.steps // 5)
-        kms, _ = event_time(lambda i: B.fp4q_quantize(kspec, kv, None, kc_, ks_, kg_, ws), ksteps, 2)
-        kms_k, _ = event_time(lambda i: B.fp4q_quantize(kspec_g, kv, None, kc_, ks_, kg_, ws), ksteps, 2)
+        kms, _ = event_time(lambda i: B.fp4q_quantize(kspec, kv, None, kc_, ks_, kg_, ws), ksteps, 2,
+                            SETTLE_MS)
+        kms_k, _ = event_time(lambda i: B.fp4q_quantize(kspec_g, kv, None, kc_, ks_, kg_, ws), ksteps,
+                              2, SETTLE_MS)
         y = torch.empty_like(kv)
-        dms, _ = event_time(lambda i: B.fp4q_dequantize(kspec, kc_, ks_, kg_, kr, kc, 16, y), ksteps, 2)
+        dms, _ = event_time(lambda i: B.fp4q_dequantize(kspec, kc_, ks_, kg_, kr, kc, 16, y), ksteps, 2,
+                            SETTLE_MS)
         kmse, _ = B.fp4q_error(kspec, kv, None, kc_, ks_, kg_, ws)
         ka, kas, kag = B.quantize(kv, rotate=16)
         kmse_abs, _ = B.error(kv, ka, kas, kag, rotate=16)
