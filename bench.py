@@ -167,7 +167,7 @@ def parse():
     p.add_argument("--no-secondary", action="store_true")
     p.add_argument("--no-cpu", action="store_true",
                    help="skip the CPU oracle leg: the baseline timing and every parity sample")
-    p.add_argument("--cpu-rows", type=int, default=2048)
+    p.add_argument("--cpu-rows", type=int, default=6144)
     p.add_argument("--no-issue", action="store_true",
                    help="skip the VALU issue-cost microbenchmark (the roofline falls back to HBM)")
     return p.parse_args()

@@ -185,6 +185,47 @@ __device__ __forceinline__ void load_block(const void* __restrict__ x, int64_t b
     }
 }
 
+// The input of a grid-stride loop that handles one block per lane and
+// iteration.  With AHEAD (bf16 only) the block's raw words are loaded one
+// iteration ahead (B/2 VGPRs), so that the load's latency overlaps the
+// arithmetic on the previous block; otherwise each block is loaded in place.
+// Loading ahead pays where the extra registers do not cost a wave per SIMD.
+template <int B, bool BF16, bool AHEAD>
+struct BlockStream {
+    static constexpr bool kAhead = BF16 && AHEAD;
+    u32x4 w[kAhead ? B / 8 : 1];
+
+    // start the load of block `blk`, if it exists
+    __device__ __forceinline__ void prefetch(const void* __restrict__ x, int64_t blk, int64_t nblocks)
+    {
+        if constexpr (kAhead) {
+            if (blk < nblocks) {
+                const u32x4* p = reinterpret_cast<const u32x4*>(x) + blk * (B / 8);
+#pragma unroll
+                for (int q = 0; q < B / 8; ++q)
+                    w[q] = __builtin_nontemporal_load(p + q);
+            }
+        }
+    }
+
+    // the B elements of block `blk`, widened to f32 (loaded ahead: the block
+    // the last prefetch loaded)
+    __device__ __forceinline__ void take(const void* __restrict__ x, int64_t blk, float* v) const
+    {
+        if constexpr (kAhead) {
+#pragma unroll
+            for (int q = 0; q < B / 8; ++q) {
+                v[8 * q + 0] = bf16_lo(w[q].x); v[8 * q + 1] = bf16_hi(w[q].x);
+                v[8 * q + 2] = bf16_lo(w[q].y); v[8 * q + 3] = bf16_hi(w[q].y);
+                v[8 * q + 4] = bf16_lo(w[q].z); v[8 * q + 5] = bf16_hi(w[q].z);
+                v[8 * q + 6] = bf16_lo(w[q].w); v[8 * q + 7] = bf16_hi(w[q].w);
+            }
+        } else {
+            load_block<B, BF16>(x, blk, v);
+        }
+    }
+};
+
 template <int B>
 __device__ __forceinline__ float block_absmax(const float* v)
 {

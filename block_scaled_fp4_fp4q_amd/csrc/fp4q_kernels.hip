@@ -1097,10 +1097,14 @@ __global__ __launch_bounds__(kThreads) void mxfp4_sweep(
     __syncthreads();
     constexpr float u = 0x1p-24f;
     const int K = hi - lo + 1;
-    for (int64_t blk = (int64_t)blockIdx.x * kThreads + threadIdx.x; blk < nblocks;
-         blk += (int64_t)gridDim.x * kThreads) {
+    const int64_t stride = (int64_t)gridDim.x * kThreads;
+    int64_t blk = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+    BlockStream<32, BF16, WMSE> in; // ahead only where it costs no wave per SIMD
+    in.prefetch(x, blk, nblocks);
+    for (; blk < nblocks; blk += stride) {
         float v[32];
-        load_block<32, BF16>(x, blk, v);
+        in.take(x, blk, v);
+        in.prefetch(x, blk + stride, nblocks);
         if constexpr (ROT)
             fwht<32>(v);
         const float a = block_absmax<32>(v);
@@ -1205,17 +1209,26 @@ __global__ __launch_bounds__(kThreads) void nvfp4_foursix(
 {
     __shared__ __attribute__((aligned(16))) float root[WMSE ? kRootCols : 1]; // read as float4
     __shared__ float wsum[WMSE ? kRootCols / 16 : 1];
+    __shared__ float2 tab[128]; // per pattern: D = fl32(s S) and r = fl32(1/D)
     const float S = global_scale(partials, npart, Sp);
+    for (int c = threadIdx.x; c < 128; c += kThreads) {
+        const float D = e4m3_value((uint32_t)(c < 0x7E ? c : 0x7E)) * S;
+        tab[c] = make_float2(D, 1.0f / D);
+    }
     bool roots_in_lds = false;
     if constexpr (WMSE)
         roots_in_lds = roots_prologue(imp, blocks_per_row * 16, root, wsum);
     __syncthreads();
     const float S6 = 6.0f * S, S4 = 4.0f * S, invS = 1.0f / S;
     constexpr float u = 0x1p-24f;
-    for (int64_t blk = (int64_t)blockIdx.x * kThreads + threadIdx.x; blk < nblocks;
-         blk += (int64_t)gridDim.x * kThreads) {
+    const int64_t stride = (int64_t)gridDim.x * kThreads;
+    int64_t blk = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+    BlockStream<16, BF16, true> in;
+    in.prefetch(x, blk, nblocks);
+    for (; blk < nblocks; blk += stride) {
         float v[16];
-        load_block<16, BF16>(x, blk, v);
+        in.take(x, blk, v);
+        in.prefetch(x, blk + stride, nblocks);
         if constexpr (ROT)
             fwht<16>(v);
         const float a = block_absmax<16>(v);
@@ -1228,12 +1241,14 @@ __global__ __launch_bounds__(kThreads) void nvfp4_foursix(
             s6 = s6 < 1u ? 1u : s6;
             s4 = s4 < 1u ? 1u : s4;
             const float v6 = e4m3_value(s6), v4 = e4m3_value(s4);
-            const float D6 = v6 * S, r6 = 1.0f / D6;
+            const float2 t6 = tab[s6];
+            const float D6 = t6.x, r6 = t6.y;
             cb = s6;
             r = r6;
             if (s4 != s6) {
                 const int64_t col0 = (blk % blocks_per_row) * 16;
-                const float D4 = v4 * S, r4 = 1.0f / D4;
+                const float2 t4 = tab[s4];
+                const float D4 = t4.x, r4 = t4.y;
                 float b[16];
                 float W = 16.0f;
                 if constexpr (WMSE)
