@@ -340,24 +340,25 @@ template <bool WMSE>
 __device__ __forceinline__ float int4_est16_codes(const float* v, const float* b, float ri, uint2& words)
 {
     float F = 0.0f;
-    uint32_t lo = 0, hi = 0;
+    // q + 8, in [1, 15], as byte k of ev[w] (element 8w + 2k) or od[w]
+    // (element 8w + 2k + 1); every byte is written
+    uint32_t ev[2] = {0u, 0u}, od[2] = {0u, 0u};
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
         const float z = v[i] * ri;
-        const float q = __builtin_fmaxf(__builtin_fminf(__builtin_rintf(z), 7.0f), -7.0f);
+        const float q = __builtin_amdgcn_fmed3f(__builtin_rintf(z), -7.0f, 7.0f);
         float d;
         if constexpr (WMSE)
             d = __builtin_fmaf(-b[i], q, b[i] * z);
         else
             d = z - q;
         F = __builtin_fmaf(d, d, F);
-        const uint32_t nib = (uint32_t)(int)q & 0xFu;
-        if (i < 8)
-            lo |= nib << (4 * i);
-        else
-            hi |= nib << (4 * (i - 8));
+        uint32_t& word = (i & 1) ? od[i / 8] : ev[i / 8];
+        word = __builtin_amdgcn_cvt_pk_u8_f32(q + 8.0f, (i % 8) / 2, word);
     }
-    words = make_uint2(lo, hi);
+    // byte k of ev | od << 4 holds q + 8 of elements 2k (low nibble) and 2k+1;
+    // (q + 8) XOR 8 is q mod 16, the two's complement nibble
+    words = make_uint2((ev[0] | (od[0] << 4)) ^ 0x88888888u, (ev[1] | (od[1] << 4)) ^ 0x88888888u);
     return F;
 }
 
