@@ -224,6 +224,34 @@ def test_c4_if4_sweep(B, ref):
     assert mse <= mb
 
 
+@pytest.mark.parametrize("rotate", [0, 32])
+def test_mxfp4_exponent_window_wmse_multi_pass(B, ref, rotate):
+    # 8189 rows: 1048192 blocks, several grid-stride passes per lane (the next
+    # block is loaded one pass ahead) and a last pass that is only partly full
+    x = synth.c3()[:8189]
+    imp = np.random.default_rng(13).lognormal(0.0, 1.0, x.shape[1]).astype(np.float32)
+    codes, scales, _ = B.quantize(to_dev(x), format=B.FP4Q_MXFP4, scale_rule=B.FP4Q_SCALE_SWEEP,
+                                  objective=1, importance=to_dev(imp), rotate=rotate)
+    want = ref.quantize(x, fmt=ref.MXFP4, rule=ref.SWEEP, objective=ref.WMSE, importance=imp,
+                        window=(0, 1), rotate=rotate, nthreads=THREADS)
+    assert np.array_equal(scales.cpu().numpy(), want["scales"])
+    assert np.array_equal(codes.cpu().numpy(), want["codes"])
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_four_over_six_mse_multi_pass(B, ref, c2data, dtype):
+    # 7001 rows of the c2 weight: 1792256 blocks, several passes per lane and
+    # a partly full last one
+    x = c2data[0][:7001]
+    if dtype == "f32":
+        x = synth.bf16_bits_to_f32(x)
+    codes, scales, gs = B.quantize(to_dev(x), scale_rule=B.FP4Q_SCALE_FOUR_OVER_SIX)
+    want = ref.quantize(x, rule=ref.FOUR_SIX, nthreads=THREADS)
+    assert gs.item() == np.float32(want["S"])
+    assert np.array_equal(scales.cpu().numpy(), want["scales"])
+    assert np.array_equal(codes.cpu().numpy(), want["codes"])
+
+
 @pytest.mark.parametrize("fmt,group", [("nvfp4", 8), ("mxfp4", 8)])
 def test_relaxed_full(B, ref, c2data, fmt, group):
     x = c2data[0] if fmt == "nvfp4" else synth.c3()
