@@ -1,5 +1,7 @@
 // valu_issue.hip -- issue cost of the VALU instructions the quantizers are
-// built from, measured on the device this runs on.
+// built from, measured on the device this runs on, and of two that a cheaper
+// error estimate would need (a decode to packed f16 and a binary32 fma with
+// an f16 operand).
 //
 // Each kernel keeps eight independent dependency chains per lane and runs
 // eight waves per SIMD, so the SIMD always has an instruction ready and the
@@ -24,7 +26,9 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kChains = 8;
 
-enum Kind { kFma32, kMul32, kEncode, kDecodeXor, kXor, kFma64 };
+enum Kind { kFma32, kMul32, kEncode, kDecodeXor, kXor, kFma64, kDecodeF16Xor, kFmaMix };
+
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 
 template <int KIND>
 __global__ __launch_bounds__(kThreads) void chains(uint32_t* __restrict__ out, uint64_t* __restrict__ clk,
@@ -55,6 +59,14 @@ __global__ __launch_bounds__(kThreads) void chains(uint32_t* __restrict__ out, u
             if constexpr (KIND == kDecodeXor) {
                 const auto t = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(u[i], 1.0f, 0);
                 u[i] ^= __float_as_uint(t[0]);
+            }
+            if constexpr (KIND == kDecodeF16Xor) { // decode to two packed f16 values
+                const half2_t t = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(u[i], 1.0f, 0);
+                u[i] ^= __builtin_bit_cast(uint32_t, t);
+            }
+            if constexpr (KIND == kFmaMix) { // binary32 fma with one f16 operand
+                const half2_t t = __builtin_bit_cast(half2_t, __float_as_uint(f[(i + 1) % kChains]));
+                f[i] = __builtin_fmaf(g[i], (float)t[1], f[i]);
             }
             if constexpr (KIND == kXor)
                 u[i] ^= u[(i + 1) % kChains];
@@ -161,13 +173,16 @@ int main()
     const double dx = cost<kDecodeXor>(s, iters, 20, 1.0);
     const double x = cost<kXor>(s, iters, 20, 1.0);
     const double f64 = cost<kFma64>(s, iters / 4, 20, 1.0);
-    if (fma < 0.0 || mul < 0.0 || enc < 0.0 || dx < 0.0 || x < 0.0 || f64 < 0.0)
+    const double dhx = cost<kDecodeF16Xor>(s, iters, 20, 1.0);
+    const double mix = cost<kFmaMix>(s, iters, 20, 1.0);
+    if (fma < 0.0 || mul < 0.0 || enc < 0.0 || dx < 0.0 || x < 0.0 || f64 < 0.0 || dhx < 0.0 || mix < 0.0)
         return 1;
     printf("{\"device\": \"%s\", \"simds\": %d, \"clock_ghz_fma32\": %.3f, \"clock_ghz_encode\": %.3f, "
            "\"cycles_per_wave64_instr\": {\"v_fma_f32\": %.3f, \"v_mul_f32\": %.3f, "
            "\"v_cvt_scalef32_pk_fp4_f32\": %.3f, \"v_cvt_scalef32_pk_f32_fp4\": %.3f, "
-           "\"v_xor_b32\": %.3f, \"v_fma_f64\": %.3f}}\n",
-           p.gcnArchName, s.simds, fma_clk * 1e-9, enc_clk * 1e-9, fma, mul, enc, dx - x, x, f64);
+           "\"v_xor_b32\": %.3f, \"v_fma_f64\": %.3f, \"v_cvt_scalef32_pk_f16_fp4\": %.3f, "
+           "\"v_fma_mix_f32\": %.3f}}\n",
+           p.gcnArchName, s.simds, fma_clk * 1e-9, enc_clk * 1e-9, fma, mul, enc, dx - x, x, f64, dhx - x, mix);
     (void)hipFree(s.out);
     (void)hipFree(s.clk);
     return 0;
