@@ -39,8 +39,9 @@
  * then be NULL, and a computed global scale is 1.
  *
  * Preconditions (not checked, results unspecified otherwise): inputs are
- * finite; a caller-supplied global scale is a normal fp32 in
- * [2^-117, 2^119]; output buffers do not overlap inputs.
+ * finite; importance weights are finite and non-negative (zero allowed); a
+ * caller-supplied global scale is a normal fp32 in [2^-117, 2^119]; output
+ * buffers do not overlap inputs.
  */
 #ifndef FP4Q_H
 #define FP4Q_H
