@@ -1395,6 +1395,30 @@ __global__ __launch_bounds__(kThreads) void if4_sweep(
     }
 }
 
+// the eight codes of v[0..7] * r, r = fl32(1 / D_q).  When D_q is below
+// 2^-128, r is +inf: every nonzero element saturates, and a zero element
+// keeps a sign-only code as |x| / D_q = 0 does (0 * inf would be NaN, which
+// the conversion turns into the saturated code)
+__device__ __forceinline__ uint32_t relaxed_word(const float* v, float r)
+{
+    float y[8];
+    if (r == __builtin_huge_valf()) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+            y[j] = v[j] == 0.0f ? v[j] : v[j] * r;
+    } else {
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+            y[j] = v[j] * r;
+    }
+    uint32_t wv = 0;
+    wv = fp4_pack2<0>(wv, y[0], y[1]);
+    wv = fp4_pack2<1>(wv, y[2], y[3]);
+    wv = fp4_pack2<2>(wv, y[4], y[5]);
+    wv = fp4_pack2<3>(wv, y[6], y[7]);
+    return wv;
+}
+
 // FOCUS deploy-side encode: codes from the relaxed step D_q = fl32(D c)
 // (one coefficient per GROUP elements), the stored scale S_dq unchanged
 // (FOCUS page, Method 2: S_q = S_dq c_i; Method 3: c_k per sub-block of 8)
@@ -1446,12 +1470,7 @@ __global__ __launch_bounds__(kThreads) void relaxed_quant(
             // one coefficient covers GROUP >= 8 consecutive elements
             const float cg = c[(8 * q) / GROUP];
             const float r = (D == 0.0f) ? 0.0f : 1.0f / (D * cg); // a zero step keeps signs only
-            uint32_t wv = 0;
-            wv = fp4_pack2<0>(wv, v[8 * q + 0] * r, v[8 * q + 1] * r);
-            wv = fp4_pack2<1>(wv, v[8 * q + 2] * r, v[8 * q + 3] * r);
-            wv = fp4_pack2<2>(wv, v[8 * q + 4] * r, v[8 * q + 5] * r);
-            wv = fp4_pack2<3>(wv, v[8 * q + 6] * r, v[8 * q + 7] * r);
-            wds[q] = wv;
+            wds[q] = relaxed_word(v + 8 * q, r);
         }
         if constexpr (B == 16)
             reinterpret_cast<uint2*>(codes)[blk] = make_uint2(wds[0], wds[1]);
@@ -1515,12 +1534,7 @@ __global__ __launch_bounds__(kThreads) void relaxed_quant_lanes(
         }
         const float cg = coef[blk * NG + (8 * s) / GROUP];
         const float r = (D == 0.0f) ? 0.0f : 1.0f / (D * cg); // a zero step keeps signs only
-        uint32_t wv = 0;
-        wv = fp4_pack2<0>(wv, v[0] * r, v[1] * r);
-        wv = fp4_pack2<1>(wv, v[2] * r, v[3] * r);
-        wv = fp4_pack2<2>(wv, v[4] * r, v[5] * r);
-        wv = fp4_pack2<3>(wv, v[6] * r, v[7] * r);
-        codes[q] = wv; // codes holds nblocks * L words
+        codes[q] = relaxed_word(v, r); // codes holds nblocks * L words
         if constexpr (!GIVEN)
             if (s == 0)
                 scales[blk] = (uint8_t)byte;

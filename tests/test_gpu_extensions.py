@@ -265,3 +265,26 @@ def test_wide_importance_vector(B, ref):
     compare(B, ref, x, B.FP4Q_IF4, B.FP4Q_SCALE_SWEEP, 1, window=(-3, 7), imp=imp)
     compare(B, ref, x, B.FP4Q_MXFP4, B.FP4Q_SCALE_SWEEP, 1, window=(0, 1), imp=imp)
     compare(B, ref, x, B.FP4Q_MXFP4, B.FP4Q_SCALE_SWEEP, 1, window=(-1, 2), rotate=32, imp=imp)
+
+
+def test_relaxed_infinite_reciprocal(B, ref):
+    # given steps so small that D c is below 2^-128: r = fl(1/(D c)) is +inf,
+    # so a zero element would give 0 * inf; its code must stay sign-only,
+    # as for |x| / S_q = 0, and every nonzero element saturates
+    rng = np.random.default_rng(95)
+    x = rng.standard_normal((3, 128)).astype(np.float32)
+    x[0, ::3] = 0.0
+    x[1, 1::4] = -0.0
+    x[2] *= np.float32(2.0 ** -140)
+    for f, fo, blk in ((B.FP4Q_MXFP4, ref.MXFP4, 32), (B.FP4Q_NVFP4, ref.NVFP4, 16)):
+        for group in (8, blk):
+            coef = np.full((3, 128 // group), 0.25, np.float32)
+            coef[:, ::2] = 1.0  # finite reciprocals beside infinite ones
+            scales = np.full(3 * 128 // blk, 0 if f == B.FP4Q_MXFP4 else 1, np.uint8)
+            S = 2.0 ** -117 if f == B.FP4Q_NVFP4 else None
+            for xin in (x, synth.f32_to_bf16_bits(x)):
+                codes, sc, _ = B.quantize_relaxed(to_dev(xin), to_dev(coef), group, format=f,
+                                                  scales=to_dev(scales), global_scale=S)
+                torch.cuda.synchronize()
+                want = ref.quantize_relaxed(xin, coef, group, fmt=fo, global_scale=S, scales=scales)
+                assert np.array_equal(codes.cpu().numpy(), want["codes"]), (f, group, xin.dtype)

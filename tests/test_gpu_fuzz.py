@@ -113,3 +113,61 @@ def test_random_configuration(B, ref, case):
         yw = ref.dequantize(want["codes"], want["scales"], want.get("S"), rows, cols, fmt=ofmt,
                             unrotate=c["rotate"])
         assert np.array_equal(y.cpu().numpy().view(np.uint32), np.asarray(yw, np.float32).view(np.uint32))
+
+
+@pytest.mark.parametrize("case", range(48))
+def test_random_relaxed(B, ref, case):
+    """FOCUS deploy encode: format, coefficient group, given or computed
+    scale bytes and global scale, dtype, shape and values drawn per case."""
+    rng = np.random.default_rng(5000 + case)
+    fmt = ["nvfp4", "mxfp4"][int(rng.integers(0, 2))]
+    block = 32 if fmt == "mxfp4" else 16
+    group = [8, block][int(rng.integers(0, 2))]
+    rows, cols = int(rng.integers(1, 41)), block * int(rng.integers(1, 41))
+    x, kind = values(rng, rows, cols, block)
+    if rng.random() < 0.5:
+        x = synth.f32_to_bf16_bits(x)
+    coef = rng.lognormal(0.0, 0.1, (rows, cols // group)).astype(np.float32)
+    given_scales = None
+    if rng.random() < 0.3:
+        top = 0xFE if fmt == "mxfp4" else 0x7E
+        given_scales = rng.integers(0, top + 1, rows * cols // block).astype(np.uint8)
+    given_S = None
+    if fmt == "nvfp4" and rng.random() < 0.3:
+        xf = synth.bf16_bits_to_f32(x) if x.dtype == np.uint16 else x
+        g = float(np.abs(xf).max()) / 1536.0 * 2.0 ** rng.uniform(-4, 4)
+        given_S = float(np.float32(min(max(g, 2.0 ** -117), 2.0 ** 119)))
+    print(f"case {case}: {fmt} group {group} shape {x.shape} {x.dtype} kind {kind} "
+          f"scales given {given_scales is not None} S {given_S}", flush=True)
+    bfmt = B.FP4Q_MXFP4 if fmt == "mxfp4" else B.FP4Q_NVFP4
+    codes, scales, gs = B.quantize_relaxed(
+        to_dev(x), to_dev(coef), group, format=bfmt,
+        scales=None if given_scales is None else to_dev(given_scales), global_scale=given_S)
+    torch.cuda.synchronize()
+    want = ref.quantize_relaxed(x, coef, group, fmt=ref.MXFP4 if fmt == "mxfp4" else ref.NVFP4,
+                                global_scale=given_S, scales=given_scales)
+    if fmt == "nvfp4":
+        assert gs.cpu().numpy()[0] == np.float32(want["S"])
+    assert np.array_equal(scales.cpu().numpy(), want["scales"])
+    assert np.array_equal(codes.cpu().numpy(), want["codes"])
+
+
+@pytest.mark.parametrize("case", range(32))
+def test_random_error(B, ref, case):
+    """MSE and WMSE of a random configuration's quantization against the
+    oracle's binary64 sums (1e-10 relative: only the order of the sums differs)."""
+    c = draw(9000 + case, B)
+    bfmt = {"nvfp4": B.FP4Q_NVFP4, "mxfp4": B.FP4Q_MXFP4, "if4": B.FP4Q_IF4}[c["fmt"]]
+    ofmt = {"nvfp4": ref.NVFP4, "mxfp4": ref.MXFP4, "if4": ref.IF4}[c["fmt"]]
+    x, imp = c["x"], c["imp"]
+    xd = to_dev(x)
+    codes, scales, gs = B.quantize(xd, format=bfmt, scale_rule=c["rule"], objective=c["objective"],
+                                   window=c["window"], rotate=c["rotate"],
+                                   importance=to_dev(imp) if c["objective"] == 1 else None,
+                                   global_scale=c["given"])
+    got = B.error(xd, codes, scales, gs, format=bfmt, rotate=c["rotate"], importance=to_dev(imp))
+    S = float(gs.cpu().numpy()[0]) if c["fmt"] != "mxfp4" else None
+    want = ref.error(x, codes.cpu().numpy(), scales.cpu().numpy(), S, fmt=ofmt, rotate=c["rotate"],
+                     importance=imp)
+    for g, w in zip(got, want):
+        assert g == pytest.approx(w, rel=1e-10, abs=1e-300)
