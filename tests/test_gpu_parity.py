@@ -137,6 +137,25 @@ def test_given_global_scale(B, ref):
     run_case(B, ref, "if4", 0, 0, 16, x, imp, given=0.01)
 
 
+def test_given_scale_extremes(B, ref):
+    # the ends of the allowed global scale: at S = 2^-117 large elements give
+    # y = |x| r = +inf (saturating codes, overflowing estimates, exact path),
+    # at S = 2^119 small elements underflow to zero codes
+    rng = np.random.default_rng(9)
+    x = rng.standard_t(3, (7, 128)).astype(np.float32)
+    x[0] *= np.float32(1e36)  # the 16-point Hadamard of the block stays finite
+    x[1] *= np.float32(1e-30)
+    x[2, :16] = 0.0
+    x[3] = x[3] * np.float32(1e20) + np.float32(1.0)
+    imp = rng.lognormal(0, 1, 128).astype(np.float32)
+    for S in (2.0 ** -117, 2.0 ** 119):
+        for fmt, rule, obj in (("nvfp4", 0, 0), ("nvfp4", 1, 0), ("nvfp4", 1, 1), ("if4", 0, 0),
+                               ("if4", 0, 1), ("if4", 1, 0)):
+            for rot in (0, 16):
+                run_case(B, ref, fmt, rule, obj, rot, x, imp, given=S)
+        run_case(B, ref, "nvfp4", 2, 1, 0, x, imp, given=S)
+
+
 def test_edge_blocks(B, ref):
     # zeros, signed zeros, tiny blocks (subnormal and clamped E4M3 scales),
     # exact midpoints, one spike, and the block holding the maximum
