@@ -80,7 +80,10 @@ def draw(seed, B):
         imp[rng.random(cols) < 0.3] = 0.0
     given = None
     if fmt != "mxfp4" and rng.random() < 0.3:
-        g = float(np.abs(x).max()) / 1536.0 * 2.0 ** rng.uniform(-4, 4)
+        if rng.random() < 0.5:  # near the computed scale
+            g = float(np.abs(x).max()) / 1536.0 * 2.0 ** rng.uniform(-4, 4)
+        else:  # anywhere in the allowed range
+            g = 2.0 ** rng.uniform(-117, 119)
         given = float(np.float32(min(max(g, 2.0 ** -117), 2.0 ** 119)))
     return dict(fmt=fmt, rule=rule, objective=objective, rotate=rotate, window=window,
                 x=synth.f32_to_bf16_bits(x) if bf16 else x, imp=imp, given=given, kind=kind)
@@ -127,7 +130,7 @@ def test_random_relaxed(B, ref, case):
     x, kind = values(rng, rows, cols, block)
     if rng.random() < 0.5:
         x = synth.f32_to_bf16_bits(x)
-    coef = rng.lognormal(0.0, 0.1, (rows, cols // group)).astype(np.float32)
+    coef = rng.lognormal(0.0, [0.1, 1.5][int(rng.integers(0, 2))], (rows, cols // group)).astype(np.float32)
     given_scales = None
     if rng.random() < 0.3:
         top = 0xFE if fmt == "mxfp4" else 0x7E
@@ -136,6 +139,8 @@ def test_random_relaxed(B, ref, case):
     if fmt == "nvfp4" and rng.random() < 0.3:
         xf = synth.bf16_bits_to_f32(x) if x.dtype == np.uint16 else x
         g = float(np.abs(xf).max()) / 1536.0 * 2.0 ** rng.uniform(-4, 4)
+        if rng.random() < 0.5:
+            g = 2.0 ** rng.uniform(-117, 119)
         given_S = float(np.float32(min(max(g, 2.0 ** -117), 2.0 ** 119)))
     print(f"case {case}: {fmt} group {group} shape {x.shape} {x.dtype} kind {kind} "
           f"scales given {given_scales is not None} S {given_S}", flush=True)
