@@ -2,7 +2,7 @@
 window, rotation, dtype, given or computed global scale, shape and value
 distribution drawn per case, so that combinations the enumerated parity
 tests do not name are covered too.  Bar: codes, scale bytes and the global
-scale bit-exact; dequantized values bit-exact on every fourth case."""
+scale bit-exact; dequantized values (binary32 or bf16) bit-exact on every fourth case."""
 import numpy as np
 import pytest
 import torch
@@ -110,12 +110,17 @@ def test_random_configuration(B, ref, case):
     bad = np.nonzero(got_s != want["scales"])[0]
     assert bad.size == 0, f"{bad.size} scale mismatches, first blocks {bad[:5]}"
     assert np.array_equal(codes.cpu().numpy(), want["codes"])
-    if case % 4 == 0:
+    if case % 4 == 0:  # dequantize, binary32 or (every other time) bf16 output
         rows, cols = x.shape
-        y = B.dequantize(codes, scales, gs, rows, cols, format=bfmt, unrotate=c["rotate"])
+        bf16_out = case % 8 == 4
+        y = B.dequantize(codes, scales, gs, rows, cols, format=bfmt, unrotate=c["rotate"],
+                         dtype=torch.bfloat16 if bf16_out else torch.float32)
         yw = ref.dequantize(want["codes"], want["scales"], want.get("S"), rows, cols, fmt=ofmt,
-                            unrotate=c["rotate"])
-        assert np.array_equal(y.cpu().numpy().view(np.uint32), np.asarray(yw, np.float32).view(np.uint32))
+                            unrotate=c["rotate"], out_dtype=ref.BF16 if bf16_out else ref.F32)
+        if bf16_out:
+            assert np.array_equal(y.view(torch.int16).cpu().numpy().view(np.uint16), yw)
+        else:
+            assert np.array_equal(y.cpu().numpy().view(np.uint32), np.asarray(yw, np.float32).view(np.uint32))
 
 
 @pytest.mark.parametrize("case", range(48))
