@@ -380,9 +380,9 @@ def extensions(args, B, synth, dev, x2, imp, ws, x2_h, imp_h):
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one MI355X only: this build has no multi-GPU path "
-              "(the quantizer shards by rows with one all-reduce(max) of the global "
-              "scale; see DESIGN.md).  Run with --gpus 1.", file=sys.stderr)
+        print("bench.py measures one MI355X only: there is no multi-GPU path (the "
+              "quantizer would shard by rows with one all-reduce(max) of the global "
+              "scale).  Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
 
     # VALU issue costs first, in a child process, before this one opens the GPU
