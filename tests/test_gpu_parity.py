@@ -277,3 +277,35 @@ def test_graph_capture_replays(B, ref):
         torch.cuda.synchronize()
         assert torch.equal(c, ce) and torch.equal(s, se) and torch.equal(g, ge)
         assert torch.equal(y.view(torch.int16), ye.view(torch.int16))
+
+
+def test_base_scale_rounding_boundaries(B, ref):
+    # Block maxima placed so that t = a / fl(6 S) falls on every E4M3 midpoint
+    # (ties go to the even pattern) and one binary32 step to either side, in
+    # the subnormal range and at the saturation boundary; MXFP4 maxima at and
+    # just below every power of two the OCP exponent can see.  S = 2^-10 makes
+    # fl(6 S) = 6 2^-10 and t = m exactly for a = 6 2^-10 m.
+    vals = [ref.lib().fp4q_ref_e4m3_value(b) for b in range(0x7F)]
+    ts = []
+    for lo, hi in zip(vals[:-1], vals[1:]):
+        mid = np.float32((np.float64(lo) + np.float64(hi)) / 2)
+        ts += [mid, np.nextafter(mid, np.float32(0)), np.nextafter(mid, np.float32(1e9))]
+    ts += [np.float32(448.0), np.float32(464.0), np.float32(480.0), np.float32(1e6),
+           np.float32(2.0 ** -10), np.float32(2.0 ** -11)]
+    S = np.float32(2.0 ** -10)
+    a = np.array(ts, np.float64) * 6.0 * float(S)
+    rng = np.random.default_rng(21)
+    x = (rng.uniform(-1, 1, (len(a), 16)) * a[:, None]).astype(np.float32)
+    x[np.arange(len(a)), rng.integers(0, 16, len(a))] = a.astype(np.float32)  # the block maximum
+    assert np.all(np.abs(x).max(axis=1) == a.astype(np.float32))
+    for fmt, rule in (("nvfp4", 0), ("nvfp4", 1), ("if4", 0)):
+        run_case(B, ref, fmt, rule, 0, 0, x, None, given=float(S))
+    # MXFP4: maxima 2^k and the float just below, k over the whole exponent range
+    ks = np.arange(-140, 128)
+    m = np.concatenate([np.ldexp(np.float32(1.0), ks).astype(np.float32),
+                        np.nextafter(np.ldexp(np.float32(1.0), ks).astype(np.float32), np.float32(0))])
+    m = m[np.isfinite(m) & (m > 0)]
+    xm = (rng.uniform(-1, 1, (len(m), 32)) * m[:, None].astype(np.float64)).astype(np.float32)
+    xm[np.arange(len(m)), rng.integers(0, 32, len(m))] = m
+    for rule in (0, 1):
+        run_case(B, ref, "mxfp4", rule, 0, 0, xm, None)
