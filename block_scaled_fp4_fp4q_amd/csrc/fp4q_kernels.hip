@@ -369,6 +369,23 @@ __device__ __forceinline__ uint4 fp4_encode32(const float* v, float r)
     return make_uint4(lo.x, lo.y, hi.x, hi.y);
 }
 
+// the 32 sign|magnitude nibbles of E2M1(y[i] / P) for a power of two P, which
+// the conversion applies exactly
+__device__ __forceinline__ uint4 fp4_encode32_scaled(const float* y, float P)
+{
+    uint32_t w[4];
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+        uint32_t c = __builtin_nondeterministic_value(0u); // every byte is written
+        c = fp4_pack2_scaled<0>(c, y[8 * g + 0], y[8 * g + 1], P);
+        c = fp4_pack2_scaled<1>(c, y[8 * g + 2], y[8 * g + 3], P);
+        c = fp4_pack2_scaled<2>(c, y[8 * g + 4], y[8 * g + 5], P);
+        c = fp4_pack2_scaled<3>(c, y[8 * g + 6], y[8 * g + 7], P);
+        w[g] = c;
+    }
+    return make_uint4(w[0], w[1], w[2], w[3]);
+}
+
 // ---------------------------------------------------------------------------
 // NVFP4 AbsMax
 // ---------------------------------------------------------------------------
@@ -1027,7 +1044,10 @@ __device__ __forceinline__ double mx_error32(const float* v, const float* w, int
     double E = 0.0;
 #pragma unroll
     for (int i = 0; i < 32; ++i) {
-        const float a = __builtin_fabsf(v[i]);
+        float a = __builtin_fabsf(v[i]);
+        // treated as redefined here, so that a caller's loop over exponents
+        // does not keep all 32 widened values live (64 VGPRs) across it
+        asm volatile("" : "+v"(a));
         const float xh = e2m1_q(a * r) * D;
         const double d = (double)a - (double)xh;
         double t = d * d;
@@ -1112,7 +1132,10 @@ __global__ __launch_bounds__(kThreads) void mxfp4_sweep(
         const int e0 = mx_exponent(a);
         const int64_t col0 = (blk % blocks_per_row) * 32;
         int eb = 1000; // chosen exponent; 1000 = undecided
-        // fast path: no clamping, and 6 * 2^e of the top exponent finite
+        uint4 out = make_uint4(0u, 0u, 0u, 0u);
+        // fast path: no clamping, and 6 * 2^e of the top exponent finite.  It
+        // works on y = v 2^-e_lo alone (exact), so v is dead from here on and
+        // the rare exact path below loads the block again.
         if (a != 0.0f && K <= 16 && e0 + lo >= -127 && e0 + hi <= 125) {
             const int el = e0 + lo;
             const float rl = pow2f(-el);
@@ -1172,8 +1195,15 @@ __global__ __launch_bounds__(kThreads) void mxfp4_sweep(
                 if (same)
                     eb = el;
             }
+            // codes of v 2^-eb = y / 2^(eb - el): the conversion applies the
+            // power-of-two scale exactly
+            if (eb != 1000)
+                out = fp4_encode32_scaled(y, pow2f(eb - el));
         }
         if (eb == 1000) { // exact binary64 search over the clamped window
+            load_block<32, BF16, false>(x, blk, v);
+            if constexpr (ROT)
+                fwht<32>(v);
             float w[32];
             if constexpr (WMSE)
                 load_weights32(imp, col0, w);
@@ -1192,8 +1222,9 @@ __global__ __launch_bounds__(kThreads) void mxfp4_sweep(
                 }
                 eprev = e;
             }
+            out = fp4_encode32(v, pow2f(-eb));
         }
-        codes[blk] = fp4_encode32(v, pow2f(-eb));
+        codes[blk] = out;
         scales[blk] = (uint8_t)(eb + 127);
     }
 }
