@@ -340,25 +340,33 @@ template <bool WMSE>
 __device__ __forceinline__ float int4_est16_codes(const float* v, const float* b, float ri, uint2& words)
 {
     float F = 0.0f;
-    // q + 8, in [1, 15], as byte k of ev[w] (element 8w + 2k) or od[w]
-    // (element 8w + 2k + 1); every byte is written
-    uint32_t ev[2] = {0u, 0u}, od[2] = {0u, 0u};
+    uint32_t out[2];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-        const float z = v[i] * ri;
-        const float q = __builtin_amdgcn_fmed3f(__builtin_rintf(z), -7.0f, 7.0f);
-        float d;
-        if constexpr (WMSE)
-            d = __builtin_fmaf(-b[i], q, b[i] * z);
-        else
-            d = z - q;
-        F = __builtin_fmaf(d, d, F);
-        uint32_t& word = (i & 1) ? od[i / 8] : ev[i / 8];
-        word = __builtin_amdgcn_cvt_pk_u8_f32(q + 8.0f, (i % 8) / 2, word);
+    for (int h = 0; h < 2; ++h) {
+        // q + 8, in [1, 15], as byte k of ev (element 8h + 2k) or od
+        // (element 8h + 2k + 1); every byte is written
+        uint32_t ev = 0u, od = 0u;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const int i = 8 * h + j;
+            const float z = v[i] * ri;
+            const float q = __builtin_amdgcn_fmed3f(__builtin_rintf(z), -7.0f, 7.0f);
+            float d;
+            if constexpr (WMSE)
+                d = __builtin_fmaf(-b[i], q, b[i] * z);
+            else
+                d = z - q;
+            F = __builtin_fmaf(d, d, F);
+            if (j & 1)
+                od = __builtin_amdgcn_cvt_pk_u8_f32(q + 8.0f, j / 2, od);
+            else
+                ev = __builtin_amdgcn_cvt_pk_u8_f32(q + 8.0f, j / 2, ev);
+        }
+        // byte k of ev | od << 4 holds q + 8 of elements 2k (low nibble) and
+        // 2k+1; (q + 8) XOR 8 is q mod 16, the two's complement nibble
+        out[h] = (ev | (od << 4)) ^ 0x88888888u;
     }
-    // byte k of ev | od << 4 holds q + 8 of elements 2k (low nibble) and 2k+1;
-    // (q + 8) XOR 8 is q mod 16, the two's complement nibble
-    words = make_uint2((ev[0] | (od[0] << 4)) ^ 0x88888888u, (ev[1] | (od[1] << 4)) ^ 0x88888888u);
+    words = make_uint2(out[0], out[1]);
     return F;
 }
 
