@@ -767,7 +767,9 @@ static void relax_rows(void* p, int64_t r0, int64_t r1)
             }
             for (int i = 0; i < B; ++i) {
                 int m = 0;
-                if (D != 0.0f) {
+                if (D != 0.0f && xb[i] != 0.0f) {
+                    /* a zero element keeps code 0: |x| / S_q = 0, also where
+                     * D_q < 2^-128 makes rq = +inf and |x| * rq would be NaN */
                     float c = q->coef[r * ngr + (jb * B + i) / q->group];
                     float Dq = D * c;
                     float rq = 1.0f / Dq;

@@ -257,9 +257,11 @@ def relaxed_block(xb, S, coefs, byte=None, fmt="nvfp4"):
     for x, c in zip(xb, coefs):
         x = f32(x)
         m = 0
-        if D != 0:
+        if D != 0 and x != 0:  # |x| / S_q = 0 for a zero element
             Dq = D * f32(c)
-            rq = f32(1.0) / Dq
-            m = nearest(Fr(float(abs(x) * rq)), E2M1)
+            with np.errstate(divide="ignore", over="ignore"):
+                rq = f32(1.0) / Dq  # +inf when D_q < 2^-128: every nonzero element saturates
+                y = abs(x) * rq
+            m = 7 if np.isinf(y) else nearest(Fr(float(y)), E2M1)
         nib.append((8 if np.signbit(x) else 0) | m)
     return byte, nib

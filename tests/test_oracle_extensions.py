@@ -124,6 +124,32 @@ def test_relaxed_encode_matches_exact_spec(ref, fmt, group):
         assert list(nib[b * B:(b + 1) * B]) == nb
 
 
+def test_relaxed_encode_with_infinite_reciprocal(ref):
+    # given steps with D c below 2^-128 (E8M0 byte 0, E4M3 byte 1 under the
+    # smallest allowed S): r_q = fl(1/D_q) is +inf, zero elements keep code 0
+    # (|x| / S_q = 0) and every other element saturates
+    rng = np.random.default_rng(7)
+    x = rng.standard_normal((2, 64)).astype(np.float32)
+    x[0, ::3] = 0.0
+    x[1, 1::4] = -0.0
+    x[1, 2::4] *= np.float32(2.0 ** -140)
+    for F, B, byte, S in ((ref.MXFP4, 32, 0, None), (ref.NVFP4, 16, 1, 2.0 ** -117)):
+        fmt = "mxfp4" if F == ref.MXFP4 else "nvfp4"
+        for group in (8, B):
+            coef = np.full((2, 64 // group), 0.25, np.float32)
+            coef[:, ::2] = 1.0
+            given = np.full(x.size // B, byte, np.uint8)
+            out = ref.quantize_relaxed(x, coef, group, fmt=F, scales=given, global_scale=S)
+            nib = ref.unpack_nibbles(out["codes"])
+            for b, xb in enumerate(blocks(x, B)):
+                r, jb = divmod(b, 64 // B)
+                cs = [coef[r, (jb * B + i) // group] for i in range(B)]
+                _, nb = X.relaxed_block(xb, f32(S if S else 1.0), cs, byte=byte, fmt=fmt)
+                assert list(nib[b * B:(b + 1) * B]) == nb
+            zero = x.reshape(-1) == 0
+            assert np.all(nib[zero] & 7 == 0)
+
+
 def test_relaxed_with_unit_coefficients_is_absmax(ref):
     # FOCUS initializes its coefficients to 1: S_q = S_dq, the AbsMax baseline
     x = synth.bf16_bits_to_f32(synth.c2(rows=32, cols=256, seed=4)[0])
