@@ -3,8 +3,9 @@
 One step = one fp4q_quantize call on the headline workload: NVFP4 ScaleSweep
 with importance-weighted MSE (offsets [-8, 7]) of a bf16 14336x4096 weight
 matrix (Student-t(4) * 0.02, lognormal(0,1) per-column importance), global
-scale computed on the device -- global max pass, scale finalize, sweep
-quantize.  Inputs are resident in HBM before timing starts; the step cycles
+scale computed on the device -- a pass of partial maxima, then the sweep
+quantizer, whose workgroups each reduce those maxima to S.  Inputs are
+resident in HBM before timing starts; the step cycles
 through several input copies so that no step reads data a previous step left
 in the 256 MB Infinity Cache.
 
