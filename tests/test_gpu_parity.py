@@ -309,3 +309,40 @@ def test_base_scale_rounding_boundaries(B, ref):
     xm[np.arange(len(m)), rng.integers(0, 32, len(m))] = m
     for rule in (0, 1):
         run_case(B, ref, "mxfp4", rule, 0, 0, xm, None)
+
+
+def test_concurrent_streams(B, ref):
+    # two calls in flight at once on two streams, each with its own workspace
+    # (the header's condition for concurrency), repeated; every result must
+    # equal the same call run alone
+    x1, imp1 = inputs("bf16", 96, 1024, seed=81)
+    x2, _ = inputs("bf16", 64, 768, seed=82)
+    cases = [(B.make_spec(B.FP4Q_NVFP4, B.FP4Q_SCALE_SWEEP, B.FP4Q_OBJ_WMSE, (-8, 7)), to_dev(x1), to_dev(imp1)),
+             (B.make_spec(B.FP4Q_IF4, B.FP4Q_SCALE_SWEEP, B.FP4Q_OBJ_MSE, (-3, 7)), to_dev(x2), None)]
+
+    def outputs(spec, xd):
+        n = xd.numel()
+        return (torch.empty(n // 2, dtype=torch.uint8, device=DEV),
+                torch.empty(n // spec.block, dtype=torch.uint8, device=DEV),
+                torch.empty(1, dtype=torch.float32, device=DEV))
+
+    want = []
+    for spec, xd, impd in cases:
+        ws = B.alloc_workspace(spec, *xd.shape, DEV)
+        o = outputs(spec, xd)
+        B.fp4q_quantize(spec, xd, impd, *o, ws)
+        want.append(o)
+    torch.cuda.synchronize()
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    wss = [B.alloc_workspace(spec, *xd.shape, DEV) for spec, xd, _ in cases]
+    outs = [[outputs(spec, xd) for _ in range(4)] for spec, xd, _ in cases]
+    for st in streams:
+        st.wait_stream(torch.cuda.current_stream())
+    for rep in range(4):
+        for i, (spec, xd, impd) in enumerate(cases):
+            B.fp4q_quantize(spec, xd, impd, *outs[i][rep], wss[i], stream=streams[i])
+    torch.cuda.synchronize()
+    for i in range(2):
+        for rep in range(4):
+            for got, exp in zip(outs[i][rep], want[i]):
+                assert torch.equal(got, exp), (i, rep)
