@@ -166,7 +166,9 @@ fp4q_status fp4q_quantize(const fp4q_spec* spec, const void* x, int32_t x_dtype,
  *               0x00..0xFE) and is not written.
  * Per element, with D the step of S_dq (fl32(s S), or 2^(byte-127)):
  * D_q = fl32(D c), code = E2M1 nearest to fl32(|x| fl32(1 / D_q)), ties to
- * the even code, saturating at 6; a block with D = 0 gets sign-only codes.
+ * the even code, saturating at 6; a block with D = 0 gets sign-only codes, and
+ * so does every zero element (also where D_q < 2^-128 makes fl32(1 / D_q)
+ * infinite, since |x| / D_q = 0).
  * fp4q_dequantize of the result applies S_dq, as the method intends.
  * Alignment: x 16, codes 8 (16 for MXFP4), coef 4, workspace 256 bytes. */
 fp4q_status fp4q_quantize_relaxed(const fp4q_spec* spec, const void* x, int32_t x_dtype,
