@@ -189,7 +189,8 @@ fp4q_status fp4q_dequantize(const fp4q_spec* spec, const uint8_t* codes, const u
     const bool empty = rows == 0 || cols == 0;
     if ((!empty && (!codes || !scales || !y)) || (has_gs && !empty && !global_scale))
         return FP4Q_E_NULL;
-    if (!aligned(codes, spec->block == 32 ? 16 : 8) || !aligned(y, 16))
+    if (!aligned(codes, spec->block == 32 ? 16 : 8) || !aligned(y, 16) ||
+        (has_gs && !aligned(global_scale, 4)))
         return FP4Q_E_ALIGN;
     fp4q::DequantArgs a{};
     a.format = spec->format;
@@ -223,7 +224,8 @@ fp4q_status fp4q_error(const fp4q_spec* spec, const void* x, int32_t x_dtype, in
         return FP4Q_E_NULL;
     if (ws_bytes < fp4q::kWorkspaceBytes)
         return FP4Q_E_ARG;
-    if (!aligned(x, 16) || !aligned(codes, spec->block == 32 ? 16 : 8) || !aligned(workspace, 256))
+    if (!aligned(x, 16) || !aligned(codes, spec->block == 32 ? 16 : 8) || !aligned(workspace, 256) ||
+        (has_gs && !aligned(global_scale, 4)) || !aligned(importance, 4))
         return FP4Q_E_ALIGN;
     fp4q::ErrorArgs a{};
     a.format = spec->format;

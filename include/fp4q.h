@@ -181,7 +181,8 @@ fp4q_status fp4q_quantize_relaxed(const fp4q_spec* spec, const void* x, int32_t 
  * FP4Q_BF16, 16-byte aligned): x_hat = +-value(code) * D, D = fl32(s S) for
  * NVFP4/IF4 (fl32(D * fl32(6/7)) for IF4 INT4 blocks, the 6/7 method) or
  * 2^(byte-127) for MXFP4; unrotate (0 or block) applies the block Hadamard,
- * which is its own inverse.  bf16 output is rounded to nearest even. */
+ * which is its own inverse.  bf16 output is rounded to nearest even.
+ * Alignment: y 16, codes 8 (16 for MXFP4), global_scale 4 bytes. */
 fp4q_status fp4q_dequantize(const fp4q_spec* spec, const uint8_t* codes,
                             const uint8_t* scales, const float* global_scale,
                             int64_t rows, int64_t cols, int32_t unrotate,
@@ -191,7 +192,9 @@ fp4q_status fp4q_dequantize(const fp4q_spec* spec, const uint8_t* codes,
  * out_host[0] = sum (x - x_hat)^2 / N, out_host[1] = sum w_col (x - x_hat)^2
  * / N (NaN when importance is NULL), accumulated in fp64 (ScaleSweep page,
  * Method 1: MSE and WMSE).  x_hat is the dequantized tensor, un-rotated when
- * spec->rotate is set.  Blocks until the two doubles are on the host. */
+ * spec->rotate is set.  Blocks until the two doubles are on the host.
+ * Alignment: x 16, codes 8 (16 for MXFP4), workspace 256, global_scale and
+ * importance 4 bytes. */
 fp4q_status fp4q_error(const fp4q_spec* spec, const void* x, int32_t x_dtype,
                        int64_t rows, int64_t cols, const float* importance,
                        const uint8_t* codes, const uint8_t* scales,

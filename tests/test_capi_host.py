@@ -155,6 +155,10 @@ def test_dequantize_and_error_reject_bad_arguments(L):
     assert e(C.byref(s), X, 1, 4, 64, None, CODES, SCALES, GS, WS, 10, out, None) == -2
     assert e(C.byref(s), X, 1, 4, 60, None, CODES, SCALES, GS, WS, 1 << 20, out, None) == -3
     assert e(C.byref(s), X, 4, 4, 64, None, CODES, SCALES, GS, WS, 1 << 20, out, None) == -2
+    # global scale and importance must be aligned for their binary32 loads
+    assert f(C.byref(s), CODES, SCALES, C.c_void_p(0x30002), 4, 64, 0, X, 0, None) == -6
+    assert e(C.byref(s), X, 1, 4, 64, None, CODES, SCALES, C.c_void_p(0x30002), WS, 1 << 20, out, None) == -6
+    assert e(C.byref(s), X, 1, 4, 64, C.c_void_p(0x50002), CODES, SCALES, GS, WS, 1 << 20, out, None) == -6
 
 
 def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
