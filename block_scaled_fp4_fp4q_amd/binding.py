@@ -114,11 +114,121 @@ def make_spec(format=FP4Q_NVFP4, scale_rule=FP4Q_SCALE_ABSMAX, objective=FP4Q_OB
 
 
 def _as_2d(x):
+    if not isinstance(x, torch.Tensor):
+        raise TypeError("x must be a torch tensor")
     if x.dim() < 2:
         raise ValueError("x must have at least 2 dimensions (rows, cols)")
     if not x.is_contiguous():
         raise ValueError("x must be contiguous")
     return x.reshape(-1, x.shape[-1])
+
+
+# The C ABI receives bare device pointers and cannot see a buffer's size,
+# device or type: a host tensor or a short buffer would be read or written
+# out of bounds by a kernel.  Every tensor argument is therefore checked here,
+# before the library is called.  `require_cuda` is only turned off by the
+# host-side tests of these checks.
+
+def _check_device(name, t, device, require_cuda):
+    if require_cuda and t.device.type != "cuda":
+        raise ValueError(f"{name} must be a tensor on a ROCm device, not {t.device}")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, but x is on {device}")
+
+
+def _check_tensor(name, t, dtypes, min_numel, device, require_cuda=True, optional=False):
+    """A device tensor argument: on x's device, one of `dtypes`, contiguous,
+    at least `min_numel` elements.  None passes only when `optional`."""
+    if t is None:
+        if optional:
+            return
+        raise ValueError(f"{name} is required")
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch tensor")
+    _check_device(name, t, device, require_cuda)
+    if t.dtype not in dtypes:
+        want = " or ".join(str(d) for d in dtypes)
+        raise ValueError(f"{name} has dtype {t.dtype}; expected {want}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if t.numel() < min_numel:
+        raise ValueError(f"{name} has {t.numel()} elements; at least {min_numel} are needed")
+
+
+_U8 = (torch.uint8,)
+_F32 = (torch.float32,)
+_X = (torch.float32, torch.bfloat16)
+
+
+def _needs_importance(spec):
+    return spec.objective == FP4Q_OBJ_WMSE and (spec.scale_rule != FP4Q_SCALE_ABSMAX
+                                                or spec.format == FP4Q_IF4)
+
+
+def _check_outputs(spec, rows, cols, codes, scales, global_scale, dev, require_cuda):
+    n = rows * cols
+    _check_tensor("codes", codes, _U8, n // 2, dev, require_cuda)
+    _check_tensor("scales", scales, _U8, n // spec.block, dev, require_cuda)
+    _check_tensor("global_scale", global_scale, _F32, 1, dev, require_cuda,
+                  optional=spec.format == FP4Q_MXFP4)
+
+
+def _check_workspace(spec, rows, cols, workspace, dev, require_cuda):
+    need = fp4q_workspace_bytes(spec, rows, cols)
+    _check_tensor("workspace", workspace, _U8, need, dev, require_cuda)
+
+
+def check_quantize_args(spec, x, importance, codes, scales, global_scale, workspace,
+                        require_cuda=True):
+    """Host-side checks of fp4q_quantize's tensor arguments; raises
+    ValueError/TypeError.  Returns x as a [rows, cols] view."""
+    x2 = _as_2d(x)
+    _check_device("x", x2, None, require_cuda)
+    _dtype_code(x2)
+    rows, cols = x2.shape
+    dev = x2.device
+    _check_tensor("importance", importance, _F32, cols, dev, require_cuda,
+                  optional=not _needs_importance(spec))
+    _check_outputs(spec, rows, cols, codes, scales, global_scale, dev, require_cuda)
+    _check_workspace(spec, rows, cols, workspace, dev, require_cuda)
+    return x2
+
+
+def check_relaxed_args(spec, x, coef, coef_group, codes, scales, global_scale, workspace,
+                       require_cuda=True):
+    x2 = _as_2d(x)
+    _check_device("x", x2, None, require_cuda)
+    _dtype_code(x2)
+    rows, cols = x2.shape
+    dev = x2.device
+    if coef_group <= 0:
+        raise ValueError("coef_group must be positive")
+    _check_tensor("coef", coef, _F32, rows * (cols // coef_group), dev, require_cuda)
+    _check_outputs(spec, rows, cols, codes, scales, global_scale, dev, require_cuda)
+    _check_workspace(spec, rows, cols, workspace, dev, require_cuda)
+    return x2
+
+
+def check_dequantize_args(spec, codes, scales, global_scale, rows, cols, y, require_cuda=True):
+    if not isinstance(y, torch.Tensor):
+        raise TypeError("y must be a torch tensor")
+    _check_device("y", y, None, require_cuda)
+    dev = y.device
+    _check_tensor("y", y, _X, rows * cols, dev, require_cuda)
+    _check_outputs(spec, rows, cols, codes, scales, global_scale, dev, require_cuda)
+
+
+def check_error_args(spec, x, importance, codes, scales, global_scale, workspace,
+                     require_cuda=True):
+    x2 = _as_2d(x)
+    _check_device("x", x2, None, require_cuda)
+    _dtype_code(x2)
+    rows, cols = x2.shape
+    dev = x2.device
+    _check_tensor("importance", importance, _F32, cols, dev, require_cuda, optional=True)
+    _check_outputs(spec, rows, cols, codes, scales, global_scale, dev, require_cuda)
+    _check_workspace(spec, rows, cols, workspace, dev, require_cuda)
+    return x2
 
 
 # ---------------------------------------------------------------------------
@@ -130,7 +240,7 @@ def fp4q_workspace_bytes(spec, rows, cols):
 
 
 def fp4q_quantize(spec, x, importance, codes, scales, global_scale, workspace, stream=None):
-    x2 = _as_2d(x)
+    x2 = check_quantize_args(spec, x, importance, codes, scales, global_scale, workspace)
     rows, cols = x2.shape
     st = _lib_handle().fp4q_quantize(C.byref(spec), _ptr(x2), _dtype_code(x2), rows, cols,
                                      _ptr(importance), _ptr(codes), _ptr(scales),
@@ -141,7 +251,7 @@ def fp4q_quantize(spec, x, importance, codes, scales, global_scale, workspace, s
 
 def fp4q_quantize_relaxed(spec, x, coef, coef_group, scales_given, codes, scales, global_scale,
                           workspace, stream=None):
-    x2 = _as_2d(x)
+    x2 = check_relaxed_args(spec, x, coef, coef_group, codes, scales, global_scale, workspace)
     rows, cols = x2.shape
     st = _lib_handle().fp4q_quantize_relaxed(C.byref(spec), _ptr(x2), _dtype_code(x2), rows, cols,
                                              _ptr(coef), coef_group, int(scales_given), _ptr(codes),
@@ -151,6 +261,7 @@ def fp4q_quantize_relaxed(spec, x, coef, coef_group, scales_given, codes, scales
 
 
 def fp4q_dequantize(spec, codes, scales, global_scale, rows, cols, unrotate, y, stream=None):
+    check_dequantize_args(spec, codes, scales, global_scale, rows, cols, y)
     st = _lib_handle().fp4q_dequantize(C.byref(spec), _ptr(codes), _ptr(scales),
                                        _ptr(global_scale), rows, cols, unrotate, _ptr(y),
                                        _dtype_code(y), _stream(stream))
@@ -158,7 +269,7 @@ def fp4q_dequantize(spec, codes, scales, global_scale, rows, cols, unrotate, y, 
 
 
 def fp4q_error(spec, x, importance, codes, scales, global_scale, workspace, stream=None):
-    x2 = _as_2d(x)
+    x2 = check_error_args(spec, x, importance, codes, scales, global_scale, workspace)
     rows, cols = x2.shape
     out = (C.c_double * 2)()
     st = _lib_handle().fp4q_error(C.byref(spec), _ptr(x2), _dtype_code(x2), rows, cols,
