@@ -48,23 +48,5 @@ def build(verbose=False):
     return LIB
 
 
-VALU_ISSUE = os.path.join(PKG, "valu_issue")
-
-
-def build_valu_issue(verbose=False):
-    """The VALU issue-cost microbenchmark (csrc/valu_issue.hip), a standalone
-    program that bench.py runs for its ALU roofline."""
-    tmp = VALU_ISSUE + ".tmp"
-    cmd = [HIPCC, f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-Wall",
-           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-           os.path.join(CSRC, "valu_issue.hip"), "-o", tmp]
-    if verbose:
-        print(" ".join(cmd), flush=True)
-    subprocess.run(cmd, check=True)
-    os.replace(tmp, VALU_ISSUE)
-    return VALU_ISSUE
-
-
 if __name__ == "__main__":
     print(build(verbose="-q" not in sys.argv))
-    print(build_valu_issue(verbose="-q" not in sys.argv))
