@@ -1,34 +1,37 @@
 """Benchmark of the block-scaled FP4 quantizer on one MI355X.
 
 One step = one fp4q_quantize call on the headline workload: NVFP4 ScaleSweep
-with importance-weighted MSE (offsets [-8, 7]) of a bf16 14336x4096 weight
-matrix (Student-t(4) * 0.02, lognormal(0,1) per-column importance), global
-scale computed on the device -- a pass of partial maxima, then the sweep
-quantizer, whose workgroups each reduce those maxima to S.  Inputs are
-resident in HBM before timing starts; the step cycles
-through several input copies so that no step reads data a previous step left
-in the 256 MB Infinity Cache.
+MSE (E4M3 bit-pattern offsets [-3, 7]) with a fused 16-point block Hadamard,
+of a bf16 KV-cache-shaped tensor [64, 32, 4096, 128] (2 GiB, N(0,1) times a
+lognormal(0, 0.5) scale per head, 0.1% of entries x30), global scale
+S = max|x| / (256*6) computed on the device.  The call is two kernels: a pass
+of partial maxima over the rotated tensor, then the sweep quantizer, whose
+workgroups each reduce those maxima to S.  The input is resident in HBM
+before timing starts and is 8x the 256 MB Infinity Cache, so every step
+streams it from HBM.
 
-Printed: one JSON line (rank 0).  `value` is quantized Gelem/s of the whole
-call; `roofline` is the dominant kernel (the sweep quantizer) timed alone
-with HIP events on the stream it runs on.  That kernel is bound by its
-vector-ALU work, so the roofline is the VALU's: the exact estimate of all 16
-candidates needs 48 binary32 operations, 8 FP4 encodes and 8 FP4 decodes per
-element, the conversions weighted by their issue cost relative to an FMA
-(measured by block_scaled_fp4_fp4q_amd/valu_issue, a microbenchmark run as a
-child process), against the published 157.3 TFLOP/s binary32 vector peak
-(78.6 T FMA lane-ops/s); the 8 TB/s HBM roofline of the same kernel is
-reported beside it;
-`cpu_baseline` is the CPU oracle on a bounded row sample of the same
-workload, and `parity_sample` compares the GPU's bytes on those rows with the
-oracle's; every other workload carries a `parity_sample` of its leading rows
-(about 2^18 elements) as well.  `configs` times the other workloads with their own rules (c1
-NVFP4 AbsMax and ScaleSweep MSE, c3 MXFP4 with and without a 32-point
-Hadamard, c4 IF4); `extensions` times Four Over Six, the MXFP4 exponent
-window, the IF4 pattern window and the FOCUS deploy encode.  `secondary` holds the 2 GiB
-KV-cache workload (NVFP4 ScaleSweep MSE
-[-3, 7] with a fused 16-point Hadamard; quantize and dequantize timed
-separately).  A plain 1 GiB device copy is the achievable-bandwidth yardstick.
+Printed: one JSON line.  `value` is quantized Gelem/s of the whole call.
+`roofline` is the dominant kernel (the sweep quantizer), timed alone with
+HIP events (calls with S supplied launch only that kernel, on torch's current
+stream), against the MI355X HBM peak: algorithmic bytes = 2.5625 per element
+(read bf16, write half a byte of codes and 1/16 byte of scale) x elements per
+launch / average launch time.  `roofline.traffic` is the kernel's measured
+HBM bytes per launch from the committed rocprofv3 FETCH_SIZE/WRITE_SIZE
+summary; `roofline.valu` the same kernel against the vector ALU, its binding
+resource (issue costs measured by measure/valu_issue in a child process, and
+the committed SQ counter summary).  `cpu_baseline` is the CPU oracle on a
+bounded row sample of the same workload; `parity_sample` compares the GPU's
+bytes on those rows with the oracle's.
+
+`secondary` holds the dequantize round trip of the same tensor (timed
+separately) and the NVFP4 ScaleSweep WMSE [-8, 7] weight workload (bf16
+14336x4096, Student-t(4) * 0.02, lognormal(0,1) per-column importance).
+`configs` times the other workloads with their own rules (c1 NVFP4 AbsMax and
+ScaleSweep MSE, c3 MXFP4 with and without a 32-point Hadamard, c4 IF4);
+`extensions` times Four Over Six, the MXFP4 exponent window, the IF4 pattern
+window and the FOCUS deploy encode.  Every timed workload carries a
+`parity_sample` of its leading rows.  A plain 1 GiB device copy is the
+achievable-bandwidth yardstick.
 """
 import argparse
 import json
@@ -45,20 +48,24 @@ sys.path.insert(0, ROOT)
 PEAK_HBM_GBPS = 8000.0
 METRIC = "quantized Gelem/s + achieved HBM GB/s (% of peak), NVFP4 ScaleSweep MSE"
 
-
-COUNTERS = os.path.join(ROOT, "profiles", "nvfp4_sweep_wmse_hbm_counters.md")
+HEADLINE_KERNEL = "nvfp4_sweep<bf16, rotate 16, mse, window [-3,7]>"
+HEADLINE_KEY = "nvfp4_sweep_mse_had16_bf16_kv_64x32x4096x128"
+COUNTERS = os.path.join(ROOT, "profiles", "nvfp4_sweep_mse_had16_kv_hbm_counters.md")
 VALU_COUNTERS = os.path.join(ROOT, "profiles", "nvfp4_sweep_valu_counters.md")
-VALU_ISSUE = os.path.join(ROOT, "block_scaled_fp4_fp4q_amd", "valu_issue")
+VALU_ISSUE = os.path.join(ROOT, "measure", "valu_issue")
 # published binary32 vector peak, 157.3 TFLOP/s, as FMA lane-ops/s: 256 CUs x
 # 4 SIMDs x 2.4 GHz x 32 lanes per cycle (a wave64 FMA issues in 2 cycles)
 PEAK_FP32_LANE_OPS = 157.3e12 / 2
-# per element of the sweep over 16 patterns in 8 exactly doubling pairs: per
-# pair, y = |x| r and b y (shared), two residual FMAs and two accumulating
-# FMAs (6 binary32 ops), one encode and one decode instruction (each converts
-# two elements of one candidate, two candidates per pair)
-SWEEP16_MIX = {"fp32": 48, "encode": 8, "decode": 8}
+# per element of the exact-code estimate over the 11 patterns of [-3, 7]
+# (three exactly doubling pairs and five singles, so 8 products y = |x| r),
+# each candidate one residual and one accumulating FMA, plus the 16-point
+# Hadamard (4 butterfly add/subs and one scaling); the conversions each
+# handle two elements of one candidate
+SWEEP11_HAD16_MIX = {"fp32": 8 + 11 + 11 + 5, "encode": 5.5, "decode": 5.5}
 KERNEL_SOURCES = ["block_scaled_fp4_fp4q_amd/csrc/fp4q_kernels.hip",
                   "block_scaled_fp4_fp4q_amd/csrc/fp4q_device.h"]
+KV_BYTES_PER_ELEM_KERNEL = 2.0 + 0.5 + 1.0 / 16       # read bf16, write codes + scales
+KV_BYTES_PER_ELEM_CALL = 2 * 2.0 + 0.5 + 1.0 / 16     # + the global-max read
 
 
 def kernel_source_hash():
@@ -70,42 +77,43 @@ def kernel_source_hash():
     return h.hexdigest()[:16]
 
 
-def measured_traffic():
-    """HBM bytes per launch of the sweep kernel from the committed rocprofv3
-    FETCH_SIZE/WRITE_SIZE summary, or None when the kernel sources changed
-    since those counters were taken."""
+def _profile_values(path, keys):
+    """Values `name key = v` from a committed counter summary, or None when
+    the file is missing or the kernel sources changed since it was taken."""
     import re
     try:
-        text = open(COUNTERS).read()
+        text = open(path).read()
     except OSError:
         return None
     h = re.search(r"Kernel sources sha256\[:16\] = `([0-9a-f]+)`", text)
-    t = re.search(r"traffic_bytes_per_launch \S+ = (\d+)", text)
-    if not h or not t or h.group(1) != kernel_source_hash():
+    if not h or h.group(1) != kernel_source_hash():
         return None
-    return int(t.group(1))
+    out = {}
+    for name in keys:
+        m = re.search(rf"{name} {HEADLINE_KEY} = ([0-9.eE+-]+)", text)
+        if not m:
+            return None
+        out[name] = float(m.group(1))
+    return out
+
+
+def measured_traffic():
+    """HBM bytes per launch of the headline sweep kernel (rocprofv3
+    FETCH_SIZE + WRITE_SIZE, copy-calibrated), or None when stale."""
+    v = _profile_values(COUNTERS, ["traffic_bytes_per_launch"])
+    return None if v is None else int(v["traffic_bytes_per_launch"])
 
 
 def measured_valu():
     """Executed VALU lane-ops per element, AMD's VALUBusy and the fraction of
-    the VALU's measured issue capacity used by the sweep kernel, from the
-    committed rocprofv3 SQ counter summary, or None when the kernel sources
-    changed since."""
-    import re
-    try:
-        text = open(VALU_COUNTERS).read()
-    except OSError:
+    the VALU's measured issue capacity used by the headline sweep kernel, from
+    the committed SQ counter summary, or None when stale."""
+    v = _profile_values(VALU_COUNTERS, ["lane_ops_per_elem", "valu_busy", "issue_capacity_used"])
+    if v is None:
         return None
-    h = re.search(r"Kernel sources sha256\[:16\] = `([0-9a-f]+)`", text)
-    ops = re.search(r"lane_ops_per_elem nvfp4_sweep_wmse_bf16_14336x4096 = ([0-9.]+)", text)
-    busy = re.search(r"valu_busy nvfp4_sweep_wmse_bf16_14336x4096 = ([0-9.]+)", text)
-    util = re.search(r"issue_capacity_used nvfp4_sweep_wmse_bf16_14336x4096 = ([0-9.]+)", text)
-    if not h or not ops or not busy or not util or h.group(1) != kernel_source_hash():
-        return None
-    return {"lane_ops_per_elem": float(ops.group(1)), "valu_busy": float(busy.group(1)),
-            "issue_capacity_used": float(util.group(1)),
-            "source": "profiles/nvfp4_sweep_valu_counters.md (SQ_INSTS_VALU, "
-                      "SQ_ACTIVE_INST_VALU, GRBM_GUI_ACTIVE)"}
+    v["source"] = ("profiles/nvfp4_sweep_valu_counters.md (SQ_INSTS_VALU, SQ_ACTIVE_INST_VALU, "
+                   "SQ_INSTS_VALU_CVT, GRBM_GUI_ACTIVE)")
+    return v
 
 
 def valu_issue_costs():
@@ -113,7 +121,7 @@ def valu_issue_costs():
     one SIMD, measured by the valu_issue microbenchmark in a child process; None
     when it is not built or fails."""
     if not os.path.exists(VALU_ISSUE):
-        log(f"{VALU_ISSUE} is not built: no ALU roofline (run __graft_entry__.build())")
+        log(f"{VALU_ISSUE} is not built (run __graft_entry__.build()): no VALU figures")
         return None
     try:
         r = subprocess.run([VALU_ISSUE], capture_output=True, text=True, timeout=120, check=True)
@@ -123,34 +131,34 @@ def valu_issue_costs():
         return None
 
 
-def roofline(n, ms_k, kernel_gbps, bytes_per_elem, issue):
-    """The sweep kernel against the VALU roof (its binding resource), with the
-    HBM roof beside it; the HBM roof alone when the issue costs are missing."""
-    hbm = {"bound": "hbm", "achieved": kernel_gbps, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
-           "frac": kernel_gbps / PEAK_HBM_GBPS,
-           "algorithmic_bytes_per_launch": n * bytes_per_elem}
-    common = {"kernel": "nvfp4_sweep<bf16, no rotation, wmse>", "kernel_ms": ms_k,
-              "traffic": measured_traffic(),
-              "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, "
-                              "copy-calibrated)",
-              "valu_counters": measured_valu()}
-    if issue is None:
-        return {**hbm, **common}
-    c = issue["cycles_per_wave64_instr"]
-    w_enc = c["v_cvt_scalef32_pk_fp4_f32"] / c["v_fma_f32"]
-    w_dec = c["v_cvt_scalef32_pk_f32_fp4"] / c["v_fma_f32"]
-    ops = SWEEP16_MIX["fp32"] + SWEEP16_MIX["encode"] * w_enc + SWEEP16_MIX["decode"] * w_dec
-    achieved = n * ops / (ms_k * 1e-3) / 1e12
-    peak = PEAK_FP32_LANE_OPS / 1e12
-    return {"bound": "alu", "achieved": achieved, "peak": peak,
-            "unit": "T VALU lane-ops/s (binary32 FMA equivalents)", "frac": achieved / peak,
-            **common,
-            "algorithmic_lane_ops_per_elem": ops,
-            "algorithmic_lane_ops_per_launch": n * ops,
-            "instruction_mix_per_elem": SWEEP16_MIX,
-            "conversion_weights": {"encode": w_enc, "decode": w_dec},
-            "issue_costs": issue,
-            "hbm": hbm}
+def roofline(n, ms_k, issue):
+    """The headline sweep kernel against the HBM roof, with its standing
+    against the vector ALU (the resource that binds it) beside it."""
+    achieved = n * KV_BYTES_PER_ELEM_KERNEL / (ms_k * 1e-3) / 1e9
+    out = {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+           "frac": achieved / PEAK_HBM_GBPS, "traffic": measured_traffic(),
+           "kernel": HEADLINE_KERNEL, "kernel_ms": ms_k,
+           "algorithmic_bytes_per_elem": KV_BYTES_PER_ELEM_KERNEL,
+           "elements_per_launch": n,
+           "algorithmic_bytes_per_launch": n * KV_BYTES_PER_ELEM_KERNEL,
+           "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, "
+                           "copy-calibrated)"}
+    valu = {"counters": measured_valu(), "instruction_mix_per_elem": SWEEP11_HAD16_MIX}
+    if issue is not None:
+        c = issue["cycles_per_wave64_instr"]
+        w_enc = c["v_cvt_scalef32_pk_fp4_f32"] / c["v_fma_f32"]
+        w_dec = c["v_cvt_scalef32_pk_f32_fp4"] / c["v_fma_f32"]
+        ops = (SWEEP11_HAD16_MIX["fp32"] + SWEEP11_HAD16_MIX["encode"] * w_enc
+               + SWEEP11_HAD16_MIX["decode"] * w_dec)
+        ach = n * ops / (ms_k * 1e-3) / 1e12
+        valu.update({"achieved": ach, "peak": PEAK_FP32_LANE_OPS / 1e12,
+                     "unit": "T VALU lane-ops/s (binary32 FMA equivalents)",
+                     "frac": ach / (PEAK_FP32_LANE_OPS / 1e12),
+                     "algorithmic_lane_ops_per_elem": ops,
+                     "conversion_weights": {"encode": w_enc, "decode": w_dec},
+                     "issue_costs": issue})
+    out["valu"] = valu
+    return out
 
 
 def log(*a):
@@ -164,13 +172,15 @@ def parse():
     p.add_argument("--warmup", type=int, default=200,
                    help="untimed steps first (the core clock settles over ~20-30 ms of load, "
                         "about 150 steps)")
-    p.add_argument("--copies", type=int, default=4, help="input copies cycled per step")
+    p.add_argument("--copies", type=int, default=4,
+                   help="input copies cycled per step of the (cache-sized) weight workload")
     p.add_argument("--no-secondary", action="store_true")
     p.add_argument("--no-cpu", action="store_true",
                    help="skip the CPU oracle leg: the baseline timing and every parity sample")
-    p.add_argument("--cpu-rows", type=int, default=6144)
+    p.add_argument("--cpu-rows", type=int, default=1 << 20,
+                   help="rows of the KV tensor the CPU oracle quantizes for its baseline")
     p.add_argument("--no-issue", action="store_true",
-                   help="skip the VALU issue-cost microbenchmark (the roofline falls back to HBM)")
+                   help="skip the VALU issue-cost microbenchmark (for profiler runs)")
     return p.parse_args()
 
 
@@ -378,6 +388,73 @@ def extensions(args, B, synth, dev, x2, imp, ws, x2_h, imp_h):
     return configs, out
 
 
+def near_tie_count(best, second):
+    live = best > 0
+    gap = np.where(live, (second - best) / np.where(live, best, 1), np.inf)
+    return int(np.sum(gap < 1e-6))
+
+
+def weight_workload(args, B, synth, dev):
+    """NVFP4 ScaleSweep WMSE [-8, 7] on the bf16 14336x4096 weight with
+    per-column importance: the full call and the sweep kernel alone, with the
+    error against AbsMax and a parity sample.  Returns (result, x, imp, ws,
+    x_h, imp_h) for the extension workloads that reuse the tensor."""
+    import torch
+    rows, cols = synth.SHAPES["c2"]
+    t = time.time()
+    x_h, imp_h = synth.c2()
+    log(f"generated c2 {rows}x{cols} in {time.time() - t:.1f}s")
+    n = rows * cols
+    xs = [to_dev(x_h, dev)]
+    for _ in range(args.copies - 1):   # 4 x 112 MiB: no step reads the Infinity Cache
+        xs.append(xs[0].clone())
+    imp = to_dev(imp_h, dev)
+    spec = B.make_spec(B.FP4Q_NVFP4, B.FP4Q_SCALE_SWEEP, B.FP4Q_OBJ_WMSE, (-8, 7))
+    spec_given = B.make_spec(B.FP4Q_NVFP4, B.FP4Q_SCALE_SWEEP, B.FP4Q_OBJ_WMSE, (-8, 7),
+                             global_scale_given=True)
+    ws = B.alloc_workspace(spec, rows, cols, dev)
+    outs = [(torch.empty(n // 2, dtype=torch.uint8, device=dev),
+             torch.empty(n // 16, dtype=torch.uint8, device=dev),
+             torch.empty(1, dtype=torch.float32, device=dev)) for _ in range(args.copies)]
+    steps = max(5, args.steps)
+
+    def full(i):
+        c, s_, g = outs[i % args.copies]
+        B.fp4q_quantize(spec, xs[i % args.copies], imp, c, s_, g, ws)
+
+    def given(i):
+        c, s_, g = outs[i % args.copies]
+        B.fp4q_quantize(spec_given, xs[i % args.copies], imp, c, s_, g, ws)
+
+    ms, _ = event_time(full, steps, 2, SETTLE_MS)
+    ms_k, _ = event_time(given, steps, 2, SETTLE_MS)
+    c, s_, g = outs[0]
+    B.fp4q_quantize(spec, xs[0], imp, c, s_, g, ws)
+    mse, wmse = B.fp4q_error(B.make_spec(), xs[0], imp, c, s_, g, ws)
+    ca, sa, ga = B.quantize(xs[0])
+    mse_a, wmse_a = B.error(xs[0], ca, sa, ga, importance=imp)
+    del ca, sa, ga
+    res = {"workload": "NVFP4 ScaleSweep WMSE [-8,7], bf16 weight 14336x4096 (t(4)*0.02), "
+                       "lognormal(0,1) column importance, global scale computed on device; "
+                       f"{args.copies} input copies cycled",
+           "quantize_ms": ms, "quantize_gelem_s": n / (ms * 1e-3) / 1e9,
+           "quantize_gbps": n * KV_BYTES_PER_ELEM_CALL / (ms * 1e-3) / 1e9,
+           "quantize_frac_of_peak": n * KV_BYTES_PER_ELEM_CALL / (ms * 1e-3) / 1e9 / PEAK_HBM_GBPS,
+           "sweep_kernel_ms": ms_k,
+           "sweep_kernel_gbps": n * KV_BYTES_PER_ELEM_KERNEL / (ms_k * 1e-3) / 1e9,
+           "sweep_kernel_frac_of_peak":
+               n * KV_BYTES_PER_ELEM_KERNEL / (ms_k * 1e-3) / 1e9 / PEAK_HBM_GBPS,
+           "nvfp4_sweep_wmse": wmse, "nvfp4_sweep_mse": mse,
+           "nvfp4_absmax_wmse": wmse_a, "nvfp4_absmax_mse": mse_a}
+    if not args.no_cpu:
+        res["parity_sample"] = sample_parity(x_h, spec, c, s_, g, importance=imp_h)
+    log(f"c2 WMSE: call {ms * 1e3:.1f} us, sweep kernel {ms_k * 1e3:.1f} us, "
+        f"WMSE {wmse:.4g} vs AbsMax {wmse_a:.4g}, parity {res.get('parity_sample')}")
+    x0 = xs[0]
+    del xs, outs
+    return res, x0, imp, ws, x_h, imp_h
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -399,41 +476,35 @@ def main():
     B.lib()
     log("device", torch.cuda.get_device_name(0))
 
-    # ---------------- headline: NVFP4 ScaleSweep WMSE on bf16 14336x4096 ----------------
-    rows, cols = synth.SHAPES["c2"]
+    # ---------------- headline: KV cache, ScaleSweep MSE + fused Hadamard16 ----------------
     t = time.time()
-    x_h, imp_h = synth.c2()
-    log(f"generated c2 {rows}x{cols} in {time.time() - t:.1f}s")
-    n = rows * cols
-    xs = [to_dev(x_h, dev)]
-    for _ in range(args.copies - 1):
-        xs.append(xs[0].clone())
-    imp = to_dev(imp_h, dev)
-    spec = B.make_spec(B.FP4Q_NVFP4, B.FP4Q_SCALE_SWEEP, B.FP4Q_OBJ_WMSE, (-8, 7))
-    spec_given = B.make_spec(B.FP4Q_NVFP4, B.FP4Q_SCALE_SWEEP, B.FP4Q_OBJ_WMSE, (-8, 7),
+    kv_h = synth.c5()
+    kr, kc = kv_h.shape
+    n = kr * kc
+    log(f"generated the KV tensor {kv_h.shape} in {time.time() - t:.1f}s")
+    kv = to_dev(kv_h, dev)
+    spec = B.make_spec(B.FP4Q_NVFP4, B.FP4Q_SCALE_SWEEP, B.FP4Q_OBJ_MSE, (-3, 7), rotate=16)
+    spec_given = B.make_spec(B.FP4Q_NVFP4, B.FP4Q_SCALE_SWEEP, B.FP4Q_OBJ_MSE, (-3, 7), rotate=16,
                              global_scale_given=True)
-    ws = B.alloc_workspace(spec, rows, cols, dev)
-    outs = [(torch.empty(n // 2, dtype=torch.uint8, device=dev),
-             torch.empty(n // 16, dtype=torch.uint8, device=dev),
-             torch.empty(1, dtype=torch.float32, device=dev)) for _ in range(args.copies)]
+    ws = B.alloc_workspace(spec, kr, kc, dev)
+    codes = torch.empty(n // 2, dtype=torch.uint8, device=dev)
+    scales = torch.empty(n // 16, dtype=torch.uint8, device=dev)
+    gs = torch.empty(1, dtype=torch.float32, device=dev)
 
     def step(i):
-        c, s, g = outs[i % args.copies]
-        B.fp4q_quantize(spec, xs[i % args.copies], imp, c, s, g, ws)
+        B.fp4q_quantize(spec, kv, None, codes, scales, gs, ws)
 
-    ms, wall = event_time(step, args.steps, args.warmup)
-    log(f"full call: {ms * 1e3:.1f} us/step (wall {wall:.3f}s for {args.steps})")
+    # `warmup` untimed steps, then about SETTLE_MS more of GPU time, so that
+    # the core clock has settled before the timed steps
+    ms, wall = event_time(step, args.steps, args.warmup, SETTLE_MS)
+    log(f"full call: {ms:.4f} ms/step (wall {wall:.3f}s)")
 
-    def sweep_only(i):
-        c, s, g = outs[i % args.copies]
-        B.fp4q_quantize(spec_given, xs[i % args.copies], imp, c, s, g, ws)
+    def sweep_only(i):  # S supplied (the S of the full call): only the sweep kernel runs
+        B.fp4q_quantize(spec_given, kv, None, codes, scales, gs, ws)
 
-    ms_k, _ = event_time(sweep_only, args.steps, args.warmup)
-    bytes_per_elem_kernel = 2.0 + 0.5 + 1.0 / 16       # read bf16, write codes + scales
-    bytes_per_elem_call = 2 * 2.0 + 0.5 + 1.0 / 16     # + the global-max read
-    kernel_gbps = n * bytes_per_elem_kernel / (ms_k * 1e-3) / 1e9
-    call_gbps = n * bytes_per_elem_call / (ms * 1e-3) / 1e9
-    log(f"sweep kernel alone: {ms_k * 1e3:.1f} us, {kernel_gbps:.0f} GB/s")
+    ms_k, _ = event_time(sweep_only, args.steps, args.warmup, SETTLE_MS)
+    log(f"sweep kernel alone: {ms_k:.4f} ms, "
+        f"{n * KV_BYTES_PER_ELEM_KERNEL / (ms_k * 1e-3) / 1e9:.0f} GB/s")
 
     # reference: a plain device copy of 1 GiB (read + write, larger than the
     # Infinity Cache) -- the achievable-bandwidth yardstick, and the kernel
@@ -445,13 +516,14 @@ def main():
     del ref_src, ref_dst
     log(f"device copy 1 GiB: {copy_gbps:.0f} GB/s")
 
-    # quality: ScaleSweep vs AbsMax MSE on the same tensor
-    c, s, g = outs[0]
-    B.fp4q_quantize(spec, xs[0], imp, c, s, g, ws)
-    mse_sweep, wmse_sweep = B.fp4q_error(B.make_spec(), xs[0], imp, c, s, g, ws)
-    ca, sa, ga = B.quantize(xs[0])
-    mse_abs, wmse_abs = B.error(xs[0], ca, sa, ga, importance=imp)
+    # quality: ScaleSweep vs AbsMax MSE on the same tensor (original domain)
+    B.fp4q_quantize(spec, kv, None, codes, scales, gs, ws)
+    mse_sweep, _ = B.fp4q_error(spec, kv, None, codes, scales, gs, ws)
+    ka, kas, kag = B.quantize(kv, rotate=16)
+    mse_abs, _ = B.error(kv, ka, kas, kag, rotate=16)
+    del ka, kas, kag
     torch.cuda.synchronize()
+    call_gbps = n * KV_BYTES_PER_ELEM_CALL / (ms * 1e-3) / 1e9
 
     result = {
         "metric": METRIC,
@@ -464,117 +536,77 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32",
+        "dtype": "bf16",
         "data": "synthetic",
         "config": {
-            "workload": "NVFP4 ScaleSweep WMSE [-8,7], bf16 weight 14336x4096 (t(4)*0.02), "
-                        "lognormal(0,1) column importance, global scale computed on device",
-            "rows": rows, "cols": cols, "block": 16, "input_dtype": "bf16",
-            "input_copies_cycled": args.copies,
+            "workload": "NVFP4 ScaleSweep MSE [-3,7] + fused 16-point block Hadamard, bf16 "
+                        "KV cache [64,32,4096,128] (2 GiB) viewed as [8388608,128]: N(0,1) x "
+                        "lognormal(0,0.5) per head, 0.1% of entries x30; global scale computed "
+                        "on device (partial maxima + sweep)",
+            "rows": kr, "cols": kc, "block": 16, "input_dtype": "bf16", "elements": n,
         },
         "achieved_gbps": call_gbps,
-        "device_copy_gbps": copy_gbps,
         "frac_of_peak": call_gbps / PEAK_HBM_GBPS,
-        "algorithmic_bytes_per_elem": bytes_per_elem_call,
+        "algorithmic_bytes_per_elem": KV_BYTES_PER_ELEM_CALL,
+        "device_copy_gbps": copy_gbps,
         "nvfp4_sweep_mse": mse_sweep,
-        "nvfp4_sweep_wmse": wmse_sweep,
         "nvfp4_absmax_mse": mse_abs,
-        "nvfp4_absmax_wmse": wmse_abs,
-        "roofline": roofline(n, ms_k, kernel_gbps, bytes_per_elem_kernel, issue),
+        "roofline": roofline(n, ms_k, issue),
     }
 
     # ---------------- CPU oracle on a row sample of the same workload ----------------
     if not args.no_cpu:
         from oracle import ref
         cores = len(os.sched_getaffinity(0))
-        r = min(args.cpu_rows, rows)
-        xs_h = np.ascontiguousarray(x_h[:r])
+        r = min(args.cpu_rows, kr)
+        xs_h = np.ascontiguousarray(kv_h[:r])
         t = time.perf_counter()
-        ref.quantize(xs_h, rule=ref.SWEEP, objective=ref.WMSE, importance=imp_h, nthreads=cores)
+        ref.quantize(xs_h, rule=ref.SWEEP, objective=ref.MSE, window=(-3, 7), rotate=16,
+                     nthreads=cores)
         dt = time.perf_counter() - t
         result["cpu_baseline"] = {
-            "value": r * cols / dt / 1e9, "unit": "Gelem/s", "cores": cores, "kind": "oracle",
-            "sample": f"first {r} of {rows} rows ({r * cols} elements), same quantize "
-                      f"(global max + ScaleSweep WMSE), {dt:.2f}s wall",
+            "value": r * kc / dt / 1e9, "unit": "Gelem/s", "cores": cores, "kind": "oracle",
+            "sample": f"first {r} of {kr} rows ({r * kc} elements) of the KV tensor, the same "
+                      f"quantize (global max of the rotated sample + ScaleSweep MSE [-3,7] with "
+                      f"the 16-point Hadamard), {dt:.2f}s wall on {cores} threads",
         }
-        log(f"cpu oracle: {r * cols / dt / 1e6:.2f} Melem/s on {cores} threads")
+        log(f"cpu oracle: {r * kc / dt / 1e6:.2f} Melem/s on {cores} threads")
         # the same rows re-quantized by the oracle under the GPU's global scale
-        c, s_, g = outs[0]
-        B.fp4q_quantize(spec, xs[0], imp, c, s_, g, ws)
-        torch.cuda.synchronize()
-        S = float(g.item())
-        want = ref.quantize(xs_h, rule=ref.SWEEP, objective=ref.WMSE, importance=imp_h,
+        S = float(gs.item())
+        want = ref.quantize(xs_h, rule=ref.SWEEP, objective=ref.MSE, window=(-3, 7), rotate=16,
                             global_scale=S, nthreads=cores, errors=True)
-        gs_rows = s_.cpu().numpy()[: r * cols // 16]
-        gc_rows = c.cpu().numpy()[: r * cols // 2]
-        live = want["best"] > 0
-        gap = np.where(live, (want["second"] - want["best"]) / np.where(live, want["best"], 1), np.inf)
+        gsc = scales[: r * kc // 16].cpu().numpy()
+        gco = codes[: r * kc // 2].cpu().numpy()
         result["parity_sample"] = {
-            "blocks": int(gs_rows.size),
-            "scale_mismatches": int(np.sum(gs_rows != want["scales"])),
-            "code_bytes_mismatched": int(np.sum(gc_rows != want["codes"])),
-            "oracle_near_tie_blocks": int(np.sum(gap < 1e-6)),
+            "rows": r, "blocks": int(gsc.size),
+            "scale_mismatches": int(np.sum(gsc != want["scales"])),
+            "code_bytes_mismatched": int(np.sum(gco != want["codes"])),
+            "oracle_near_tie_blocks": near_tie_count(want["best"], want["second"]),
         }
+        del want, xs_h
         log(f"parity on the sample: {result['parity_sample']}")
 
-    # ---------------- extensions: 4/6, MXFP4 exponent window, IF4 window, FOCUS ----------------
+    # ---------------- secondary: dequantize round trip, the weight workload ----------------
     if not args.no_secondary:
-        result["configs"], result["extensions"] = extensions(args, B, synth, dev, xs[0], imp, ws,
-                                                             x_h, imp_h)
-
-    # ---------------- secondary: KV cache, sweep MSE + fused Hadamard ----------------
-    if not args.no_secondary:
-        del xs, outs
-        torch.cuda.empty_cache()
-        t = time.time()
-        kv_h = synth.c5()
-        log(f"generated c5 {kv_h.shape} in {time.time() - t:.1f}s")
-        kv = to_dev(kv_h, dev)
-        kv_head = np.ascontiguousarray(kv_h[: SAMPLE_ELEMS // kv_h.shape[1]])
-        del kv_h
-        kr, kc = kv.shape
-        kn = kr * kc
-        kspec = B.make_spec(B.FP4Q_NVFP4, B.FP4Q_SCALE_SWEEP, B.FP4Q_OBJ_MSE, (-3, 7), rotate=16)
-        kspec_g = B.make_spec(B.FP4Q_NVFP4, B.FP4Q_SCALE_SWEEP, B.FP4Q_OBJ_MSE, (-3, 7), rotate=16,
-                              global_scale_given=True)
-        kc_, ks_, kg_ = (torch.empty(kn // 2, dtype=torch.uint8, device=dev),
-                         torch.empty(kn // 16, dtype=torch.uint8, device=dev),
-                         torch.empty(1, dtype=torch.float32, device=dev))
-        ksteps = max(5, args.steps // 5)
-        kms, _ = event_time(lambda i: B.fp4q_quantize(kspec, kv, None, kc_, ks_, kg_, ws), ksteps, 2,
-                            SETTLE_MS)
-        kms_k, _ = event_time(lambda i: B.fp4q_quantize(kspec_g, kv, None, kc_, ks_, kg_, ws), ksteps,
-                              2, SETTLE_MS)
         y = torch.empty_like(kv)
-        dms, _ = event_time(lambda i: B.fp4q_dequantize(kspec, kc_, ks_, kg_, kr, kc, 16, y), ksteps, 2,
-                            SETTLE_MS)
-        kmse, _ = B.fp4q_error(kspec, kv, None, kc_, ks_, kg_, ws)
-        ka, kas, kag = B.quantize(kv, rotate=16)
-        kmse_abs, _ = B.error(kv, ka, kas, kag, rotate=16)
-        del ka, kas
-        torch.cuda.synchronize()
-        result["secondary"] = {
-            "kv_cache_sweep_mse_hadamard16": {
-                "workload": "NVFP4 ScaleSweep MSE [-3,7] + fused 16-point Hadamard, bf16 KV cache "
-                            "[64,32,4096,128] (2 GiB), global scale computed on device",
-                "quantize_ms": kms,
-                "quantize_gelem_s": kn / (kms * 1e-3) / 1e9,
-                "quantize_gbps": kn * 4.5625 / (kms * 1e-3) / 1e9,
-                "quantize_frac_of_peak": kn * 4.5625 / (kms * 1e-3) / 1e9 / PEAK_HBM_GBPS,
-                "sweep_kernel_ms": kms_k,
-                "sweep_kernel_gbps": kn * 2.5625 / (kms_k * 1e-3) / 1e9,
-                "dequantize_ms": dms,
-                "dequantize_gbps": kn * 2.5625 / (dms * 1e-3) / 1e9,
-                "nvfp4_sweep_mse": kmse,
-                "nvfp4_absmax_mse": kmse_abs,
-            },
-        }
-        if not args.no_cpu:
-            # kc_, ks_, kg_ hold the last quantize of kv (S given: the S of the full call)
-            result["secondary"]["kv_cache_sweep_mse_hadamard16"]["parity_sample"] = sample_parity(
-                kv_head, kspec, kc_, ks_, kg_)
-        log(f"c5 quantize {kms:.3f} ms, sweep kernel {kms_k:.3f} ms, dequant {dms:.3f} ms, parity "
-            f"{result['secondary']['kv_cache_sweep_mse_hadamard16'].get('parity_sample')}")
+        dms, _ = event_time(lambda i: B.fp4q_dequantize(spec, codes, scales, gs, kr, kc, 16, y),
+                            max(5, args.steps // 4), 2, SETTLE_MS)
+        dgbps = n * (0.5 + 1.0 / 16 + 2.0) / (dms * 1e-3) / 1e9
+        del y
+        log(f"dequantize + un-rotate to bf16: {dms:.4f} ms, {dgbps:.0f} GB/s")
+        secondary = {"kv_cache_dequantize_unrotate_bf16": {
+            "workload": "dequantize + inverse 16-point Hadamard of the headline's codes to bf16 "
+                        "[8388608,128] (reads 0.5625, writes 2 bytes per element)",
+            "dequantize_ms": dms, "dequantize_gbps": dgbps,
+            "dequantize_frac_of_peak": dgbps / PEAK_HBM_GBPS}}
+        del kv, codes, scales
+        del kv_h
+        torch.cuda.empty_cache()
+        w, x2, imp, ws2, x2_h, imp_h = weight_workload(args, B, synth, dev)
+        secondary["nvfp4_sweep_wmse_weight_c2"] = w
+        result["secondary"] = secondary
+        result["configs"], result["extensions"] = extensions(args, B, synth, dev, x2, imp, ws2,
+                                                             x2_h, imp_h)
 
     print(json.dumps(result), flush=True)
 

@@ -18,23 +18,28 @@ ISSUE = {"device": "gfx950", "simds": 1024,
                                      "v_xor_b32": 1.5, "v_fma_f64": 4.0}}
 
 
-def test_alu_roofline_arithmetic():
-    n, ms = 1 << 20, 0.5
-    r = bench.roofline(n, ms, 1000.0, 2.5625, ISSUE)
-    assert r["bound"] == "alu"
-    # 48 binary32 ops + 8 encodes at 4 FMAs each + 8 decodes at 3 FMAs each
-    assert r["algorithmic_lane_ops_per_elem"] == pytest.approx(48 + 8 * 4 + 8 * 3)
-    assert r["achieved"] == pytest.approx(n * 104 / (ms * 1e-3) / 1e12)
-    assert r["peak"] == pytest.approx(157.3 / 2)
-    assert r["frac"] == pytest.approx(r["achieved"] / r["peak"])
-    assert r["hbm"]["frac"] == pytest.approx(1000.0 / 8000.0)
-    assert r["hbm"]["algorithmic_bytes_per_launch"] == pytest.approx(n * 2.5625)
-
-
-def test_hbm_roofline_without_issue_costs():
-    r = bench.roofline(1 << 20, 0.5, 2000.0, 2.5625, None)
+def test_hbm_roofline_arithmetic():
+    # the KV workload: 2^30 elements, 2.5625 algorithmic bytes each per launch
+    n, ms = 1 << 30, 1.0
+    r = bench.roofline(n, ms, ISSUE)
     assert r["bound"] == "hbm" and r["unit"] == "GB/s"
-    assert r["frac"] == pytest.approx(0.25)
+    assert r["algorithmic_bytes_per_launch"] == pytest.approx(n * 2.5625)
+    assert r["achieved"] == pytest.approx(n * 2.5625 / 1e-3 / 1e9)
+    assert r["peak"] == 8000.0
+    assert r["frac"] == pytest.approx(r["achieved"] / 8000.0)
+
+
+def test_valu_figures_beside_the_roofline():
+    n, ms = 1 << 20, 0.5
+    v = bench.roofline(n, ms, ISSUE)["valu"]
+    # 35 binary32 ops + 5.5 encodes at 4 FMAs each + 5.5 decodes at 3 FMAs each
+    assert v["algorithmic_lane_ops_per_elem"] == pytest.approx(35 + 5.5 * 4 + 5.5 * 3)
+    assert v["achieved"] == pytest.approx(n * 73.5 / (ms * 1e-3) / 1e12)
+    assert v["peak"] == pytest.approx(157.3 / 2)
+    assert v["frac"] == pytest.approx(v["achieved"] / v["peak"])
+    # without the microbenchmark the HBM roofline stands alone
+    r = bench.roofline(n, ms, None)
+    assert r["bound"] == "hbm" and "achieved" not in r["valu"]
 
 
 def test_more_than_one_gpu_is_refused():
