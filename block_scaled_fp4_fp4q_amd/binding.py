@@ -19,11 +19,12 @@ FP4Q_SCALE_ABSMAX, FP4Q_SCALE_SWEEP, FP4Q_SCALE_FOUR_OVER_SIX = 0, 1, 2
 FP4Q_OBJ_MSE, FP4Q_OBJ_WMSE = 0, 1
 
 STATUS = {0: "FP4Q_OK", -1: "FP4Q_E_NULL", -2: "FP4Q_E_ARG", -3: "FP4Q_E_SHAPE",
-          -4: "FP4Q_E_UNSUPPORTED", -5: "FP4Q_E_HIP", -6: "FP4Q_E_ALIGN"}
+          -4: "FP4Q_E_UNSUPPORTED", -5: "FP4Q_E_HIP", -6: "FP4Q_E_ALIGN", -7: "FP4Q_E_SCRATCH"}
 
 # every symbol include/fp4q.h declares
-EXPORTS = ("fp4q_workspace_bytes", "fp4q_quantize", "fp4q_quantize_relaxed", "fp4q_dequantize",
-           "fp4q_error", "fp4q_status_string", "fp4q_abi_version")
+EXPORTS = ("fp4q_workspace_bytes", "fp4q_quantize", "fp4q_quantize_noalloc",
+           "fp4q_quantize_relaxed", "fp4q_dequantize", "fp4q_error", "fp4q_status_string",
+           "fp4q_abi_version")
 
 
 class fp4q_spec(C.Structure):
@@ -55,6 +56,8 @@ def _lib_handle():
         L.fp4q_workspace_bytes.argtypes = [sp, i64, i64]
         L.fp4q_quantize.restype = C.c_int
         L.fp4q_quantize.argtypes = [sp, vp, i32, i64, i64, vp, vp, vp, vp, vp, sz, vp]
+        L.fp4q_quantize_noalloc.restype = C.c_int
+        L.fp4q_quantize_noalloc.argtypes = [sp, vp, i32, i64, i64, vp, vp, vp, vp, vp]
         L.fp4q_quantize_relaxed.restype = C.c_int
         L.fp4q_quantize_relaxed.argtypes = [sp, vp, i32, i64, i64, vp, i32, i32, vp, vp, vp, vp,
                                             sz, vp]
@@ -194,6 +197,21 @@ def check_quantize_args(spec, x, importance, codes, scales, global_scale, worksp
     return x2
 
 
+def check_quantize_noalloc_args(spec, x, importance, codes, scales, global_scale,
+                                require_cuda=True):
+    """fp4q_quantize's checks without the workspace (the library's own
+    static scratch serves instead)."""
+    x2 = _as_2d(x)
+    _check_device("x", x2, None, require_cuda)
+    _dtype_code(x2)
+    rows, cols = x2.shape
+    dev = x2.device
+    _check_tensor("importance", importance, _F32, cols, dev, require_cuda,
+                  optional=not _needs_importance(spec))
+    _check_outputs(spec, rows, cols, codes, scales, global_scale, dev, require_cuda)
+    return x2
+
+
 def check_relaxed_args(spec, x, coef, coef_group, codes, scales, global_scale, workspace,
                        require_cuda=True):
     x2 = _as_2d(x)
@@ -247,6 +265,17 @@ def fp4q_quantize(spec, x, importance, codes, scales, global_scale, workspace, s
                                      _ptr(global_scale), _ptr(workspace), workspace.numel(),
                                      _stream(stream))
     _check("fp4q_quantize", st)
+
+
+def fp4q_quantize_noalloc(spec, x, importance, codes, scales, global_scale, stream=None):
+    """fp4q_quantize without a workspace: the library's static per-GPU
+    scratch serves instead.  Calls that overlap on one GPU race on it."""
+    x2 = check_quantize_noalloc_args(spec, x, importance, codes, scales, global_scale)
+    rows, cols = x2.shape
+    st = _lib_handle().fp4q_quantize_noalloc(C.byref(spec), _ptr(x2), _dtype_code(x2), rows, cols,
+                                             _ptr(importance), _ptr(codes), _ptr(scales),
+                                             _ptr(global_scale), _stream(stream))
+    _check("fp4q_quantize_noalloc", st)
 
 
 def fp4q_quantize_relaxed(spec, x, coef, coef_group, scales_given, codes, scales, global_scale,

@@ -57,36 +57,11 @@ fp4q_status check_shape(int64_t rows, int64_t cols, int block)
 
 bool valid_dtype(int32_t d) { return d == FP4Q_F32 || d == FP4Q_BF16; }
 
-} // namespace
-
-extern "C" {
-
-int fp4q_abi_version(void) { return FP4Q_ABI_VERSION; }
-
-const char* fp4q_status_string(fp4q_status s)
-{
-    switch (s) {
-    case FP4Q_OK: return "ok";
-    case FP4Q_E_NULL: return "a required pointer is NULL";
-    case FP4Q_E_ARG: return "invalid argument (enum, window, rotation or workspace size)";
-    case FP4Q_E_SHAPE: return "invalid shape (negative size, or cols not a multiple of the block)";
-    case FP4Q_E_UNSUPPORTED: return "unsupported combination (block size, Four Over Six outside NVFP4, relaxed IF4 or rotation)";
-    case FP4Q_E_HIP: return "the HIP runtime refused a launch or copy";
-    case FP4Q_E_ALIGN: return "a tensor pointer is not aligned as required";
-    }
-    return "unknown status";
-}
-
-size_t fp4q_workspace_bytes(const fp4q_spec* spec, int64_t rows, int64_t cols)
-{
-    if (check_spec(spec, false) != FP4Q_OK || check_shape(rows, cols, spec->block) != FP4Q_OK)
-        return 0;
-    return fp4q::kWorkspaceBytes;
-}
-
-fp4q_status fp4q_quantize(const fp4q_spec* spec, const void* x, int32_t x_dtype, int64_t rows,
-                          int64_t cols, const float* importance, uint8_t* codes, uint8_t* scales,
-                          float* global_scale, void* workspace, size_t ws_bytes, void* stream)
+// checks of every fp4q_quantize argument except the workspace, and the
+// launch arguments they describe (workspace and stream left to the caller)
+fp4q_status check_quantize(const fp4q_spec* spec, const void* x, int32_t x_dtype, int64_t rows,
+                           int64_t cols, const float* importance, uint8_t* codes, uint8_t* scales,
+                           float* global_scale, fp4q::QuantArgs& a)
 {
     fp4q_status st = check_spec(spec, true);
     if (st != FP4Q_OK)
@@ -100,16 +75,12 @@ fp4q_status fp4q_quantize(const fp4q_spec* spec, const void* x, int32_t x_dtype,
     const bool wants_imp = spec->objective == FP4Q_OBJ_WMSE &&
                            (spec->scale_rule != FP4Q_SCALE_ABSMAX || spec->format == FP4Q_IF4);
     const bool empty = rows == 0 || cols == 0; // tensor pointers may then be NULL
-    if ((!empty && (!x || !codes || !scales)) || !workspace || (has_gs && !global_scale) ||
+    if ((!empty && (!x || !codes || !scales)) || (has_gs && !global_scale) ||
         (wants_imp && !empty && !importance))
         return FP4Q_E_NULL;
-    if (ws_bytes < fp4q::kWorkspaceBytes)
-        return FP4Q_E_ARG;
-    if (!aligned(x, 16) || !aligned(codes, spec->block == 32 ? 16 : 8) || !aligned(workspace, 256) ||
+    if (!aligned(x, 16) || !aligned(codes, spec->block == 32 ? 16 : 8) ||
         (wants_imp && !aligned(importance, 16)) || (has_gs && !aligned(global_scale, 4)))
         return FP4Q_E_ALIGN;
-
-    fp4q::QuantArgs a{};
     a.format = spec->format;
     a.rule = spec->scale_rule == FP4Q_SCALE_SWEEP ? fp4q::kSweep
            : spec->scale_rule == FP4Q_SCALE_FOUR_OVER_SIX ? fp4q::kFourSix : fp4q::kAbsMax;
@@ -126,8 +97,72 @@ fp4q_status fp4q_quantize(const fp4q_spec* spec, const void* x, int32_t x_dtype,
     a.codes = codes;
     a.scales = scales;
     a.global_scale = global_scale;
+    return FP4Q_OK;
+}
+
+} // namespace
+
+extern "C" {
+
+int fp4q_abi_version(void) { return FP4Q_ABI_VERSION; }
+
+const char* fp4q_status_string(fp4q_status s)
+{
+    switch (s) {
+    case FP4Q_OK: return "ok";
+    case FP4Q_E_NULL: return "a required pointer is NULL";
+    case FP4Q_E_ARG: return "invalid argument (enum, window, rotation or workspace size)";
+    case FP4Q_E_SHAPE: return "invalid shape (negative size, or cols not a multiple of the block)";
+    case FP4Q_E_UNSUPPORTED: return "unsupported combination (block size, Four Over Six outside NVFP4, relaxed IF4 or rotation)";
+    case FP4Q_E_HIP: return "the HIP runtime refused a launch or copy";
+    case FP4Q_E_ALIGN: return "a tensor pointer is not aligned as required";
+    case FP4Q_E_SCRATCH: return "the problem needs more scratch than fp4q_quantize_noalloc holds";
+    }
+    return "unknown status";
+}
+
+size_t fp4q_workspace_bytes(const fp4q_spec* spec, int64_t rows, int64_t cols)
+{
+    if (check_spec(spec, false) != FP4Q_OK || check_shape(rows, cols, spec->block) != FP4Q_OK)
+        return 0;
+    return fp4q::kWorkspaceBytes;
+}
+
+fp4q_status fp4q_quantize(const fp4q_spec* spec, const void* x, int32_t x_dtype, int64_t rows,
+                          int64_t cols, const float* importance, uint8_t* codes, uint8_t* scales,
+                          float* global_scale, void* workspace, size_t ws_bytes, void* stream)
+{
+    fp4q::QuantArgs a{};
+    fp4q_status st = check_quantize(spec, x, x_dtype, rows, cols, importance, codes, scales,
+                                    global_scale, a);
+    if (st != FP4Q_OK)
+        return st;
+    if (!workspace)
+        return FP4Q_E_NULL;
+    if (ws_bytes < fp4q::kWorkspaceBytes)
+        return FP4Q_E_ARG;
+    if (!aligned(workspace, 256))
+        return FP4Q_E_ALIGN;
     a.workspace = workspace;
     a.stream = static_cast<hipStream_t>(stream);
+    return fp4q::launch_quantize(a) == hipSuccess ? FP4Q_OK : FP4Q_E_HIP;
+}
+
+fp4q_status fp4q_quantize_noalloc(const fp4q_spec* spec, const void* x, int32_t x_dtype,
+                                  int64_t rows, int64_t cols, const float* importance,
+                                  uint8_t* codes, uint8_t* scales, float* global_scale,
+                                  void* stream)
+{
+    fp4q::QuantArgs a{};
+    fp4q_status st = check_quantize(spec, x, x_dtype, rows, cols, importance, codes, scales,
+                                    global_scale, a);
+    if (st != FP4Q_OK)
+        return st;
+    if (fp4q_workspace_bytes(spec, rows, cols) > (size_t)FP4Q_NOALLOC_SCRATCH_BYTES)
+        return FP4Q_E_SCRATCH;
+    a.stream = static_cast<hipStream_t>(stream);
+    if (fp4q::static_scratch(a.stream, &a.workspace) != hipSuccess)
+        return FP4Q_E_HIP;
     return fp4q::launch_quantize(a) == hipSuccess ? FP4Q_OK : FP4Q_E_HIP;
 }
 

@@ -20,6 +20,8 @@
 #include "fp4q_device.h"
 #include "fp4q_launch.h"
 
+#include <mutex>
+
 namespace fp4q {
 
 constexpr int kThreads = 256;
@@ -1756,6 +1758,51 @@ __global__ __launch_bounds__(64) void error_final(const double2* __restrict__ pa
         out[0] = a * inv_n;
         out[1] = has_imp ? b * inv_n : __builtin_nan("");
     }
+}
+
+// ---------------------------------------------------------------------------
+// static scratch of the entry point that allocates nothing
+// ---------------------------------------------------------------------------
+
+// One workspace's worth of device memory at file scope.  Every GPU the
+// library runs on holds its own copy, at its own address, until the process
+// ends.  In host code `scratch` names a host-side stand-in, not device
+// memory: kernels receive the address looked up below, never the name.
+static __device__ __align__(256) unsigned char scratch[kWorkspaceBytes];
+
+constexpr int kMaxScratchDevices = 256;
+static std::mutex scratch_lock;
+static void* scratch_addr[kMaxScratchDevices]; // per device, filled on first use
+
+hipError_t static_scratch(hipStream_t stream, void** out)
+{
+    int cur = 0;
+    hipError_t e = hipGetDevice(&cur);
+    if (e != hipSuccess)
+        return e;
+    int dev = cur;
+    if (stream != nullptr && (e = hipStreamGetDevice(stream, &dev)) != hipSuccess)
+        return e;
+    if (dev < 0 || dev >= kMaxScratchDevices)
+        return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> guard(scratch_lock);
+    if (scratch_addr[dev] == nullptr) {
+        // the symbol's address on `dev` is looked up with `dev` current
+        if (dev != cur && (e = hipSetDevice(dev)) != hipSuccess)
+            return e;
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (dev != cur) {
+            const hipError_t r = hipSetDevice(cur);
+            if (e == hipSuccess)
+                e = r;
+        }
+        if (e != hipSuccess)
+            return e;
+        scratch_addr[dev] = p;
+    }
+    *out = scratch_addr[dev];
+    return hipSuccess;
 }
 
 // ---------------------------------------------------------------------------

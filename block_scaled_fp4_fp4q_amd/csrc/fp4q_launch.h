@@ -68,6 +68,12 @@ struct RelaxArgs {
     hipStream_t stream;
 };
 
+// Device address, on the GPU that runs `stream` (the current device for the
+// null stream), of the library's static scratch array of kWorkspaceBytes:
+// the workspace of the entry point that allocates nothing.  Looked up once
+// per device and kept.
+hipError_t static_scratch(hipStream_t stream, void** out);
+
 hipError_t launch_quantize(const QuantArgs& a);
 hipError_t launch_quantize_relaxed(const RelaxArgs& a);
 hipError_t launch_dequantize(const DequantArgs& a);

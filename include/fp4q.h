@@ -25,10 +25,11 @@
  *
  * Ownership and threading.  Every tensor pointer is a DEVICE pointer owned by
  * the caller, as is the workspace; the library allocates nothing, frees
- * nothing and keeps no state between calls.  Calls are asynchronous on the
- * given stream (a hipStream_t passed as void*; NULL is the null stream)
- * except fp4q_error, which waits for its own result.  Two calls may run
- * concurrently only with separate workspaces.
+ * nothing and keeps no state between calls, apart from the static scratch of
+ * fp4q_quantize_noalloc.  Calls are asynchronous on the given stream (a
+ * hipStream_t passed as void*; NULL is the null stream) except fp4q_error,
+ * which waits for its own result.  Two calls may run concurrently only with
+ * separate workspaces (fp4q_quantize_noalloc calls: never on one GPU).
  *
  * Errors.  Every entry point returns an fp4q_status.  Argument, shape and
  * alignment errors are detected on the host before anything is launched and
@@ -53,7 +54,7 @@
 extern "C" {
 #endif
 
-#define FP4Q_ABI_VERSION 2
+#define FP4Q_ABI_VERSION 3
 
 typedef enum {
     FP4Q_OK = 0,
@@ -62,7 +63,8 @@ typedef enum {
     FP4Q_E_SHAPE = -3,       /* negative sizes or cols % block != 0          */
     FP4Q_E_UNSUPPORTED = -4, /* a combination outside the methods' scope     */
     FP4Q_E_HIP = -5,         /* the HIP runtime refused a launch or copy     */
-    FP4Q_E_ALIGN = -6        /* a tensor pointer is not aligned as required  */
+    FP4Q_E_ALIGN = -6,       /* a tensor pointer is not aligned as required  */
+    FP4Q_E_SCRATCH = -7      /* more scratch than fp4q_quantize_noalloc has  */
 } fp4q_status;
 
 typedef enum { FP4Q_NVFP4 = 0, FP4Q_MXFP4 = 1, FP4Q_IF4 = 2 } fp4q_format;
@@ -149,6 +151,27 @@ fp4q_status fp4q_quantize(const fp4q_spec* spec, const void* x, int32_t x_dtype,
                           int64_t rows, int64_t cols, const float* importance,
                           uint8_t* codes, uint8_t* scales, float* global_scale,
                           void* workspace, size_t ws_bytes, void* stream);
+
+/* fp4q_quantize for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * The arguments are fp4q_quantize's without the workspace, and the results
+ * are the same.  The scratch fp4q_quantize takes from the workspace (the
+ * partial maxima of the global-scale pass) is instead a static device array
+ * of FP4Q_NOALLOC_SCRATCH_BYTES inside the library: each GPU it runs on
+ * holds its own copy until the process ends.  The first call on a GPU looks
+ * up that array's address there; no call allocates or frees anything.
+ *   Limit: problems whose fp4q_workspace_bytes() exceeds
+ *   FP4Q_NOALLOC_SCRATCH_BYTES are refused with FP4Q_E_SCRATCH (in this
+ *   version every valid problem needs exactly that much, so none is).
+ *   Sharing: every call on one GPU uses the same array and leaves its
+ *   contents behind (nothing in it needs to start at zero).  Calls that
+ *   overlap on one GPU -- on two streams, or from two host threads -- race
+ *   on it and must be serialized by the caller. */
+#define FP4Q_NOALLOC_SCRATCH_BYTES 32768
+fp4q_status fp4q_quantize_noalloc(const fp4q_spec* spec, const void* x, int32_t x_dtype,
+                                  int64_t rows, int64_t cols, const float* importance,
+                                  uint8_t* codes, uint8_t* scales, float* global_scale,
+                                  void* stream);
 
 /* Deploy-side encode of FOCUS (FOCUS page, Method 2, coupled-relaxation
  * scaling: the quantization scale S_q = S_dq c while the stored

@@ -38,7 +38,7 @@ def test_library_exports_every_declared_symbol(L):
 
 
 def test_abi_version_and_status_strings(L):
-    assert L.fp4q_abi_version() == 2
+    assert L.fp4q_abi_version() == 3
     for st in B.STATUS:
         assert L.fp4q_status_string(st)
     assert L.fp4q_status_string(-99) == b"unknown status"
@@ -166,3 +166,17 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(B, "_LIB", None)
     with pytest.raises(ImportError):
         B.lib()
+
+
+def test_noalloc_rejects_bad_arguments_before_any_hip_call(L):
+    def qn(s, x=X, dtype=B.FP4Q_BF16, rows=4, cols=64, imp=None, codes=CODES, scales=SCALES,
+           gs=GS):
+        return L.fp4q_quantize_noalloc(C.byref(s) if s is not None else None, x, dtype, rows,
+                                       cols, imp, codes, scales, gs, None)
+    assert qn(None) == -1                                   # FP4Q_E_NULL
+    assert qn(spec(format=7)) == -2                         # FP4Q_E_ARG
+    assert qn(spec(), cols=60) == -3                        # FP4Q_E_SHAPE
+    assert qn(spec(), x=C.c_void_p(0x10008)) == -6          # FP4Q_E_ALIGN
+    assert qn(spec(), gs=None) == -1
+    assert qn(spec(scale_rule=1, objective=1)) == -1        # WMSE without importance
+    assert L.fp4q_status_string(-7) != b"unknown status"
