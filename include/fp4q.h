@@ -132,7 +132,9 @@ size_t fp4q_workspace_bytes(const fp4q_spec* spec, int64_t rows, int64_t cols);
 
 /* Quantize x [rows, cols] (dtype FP4Q_F32 or FP4Q_BF16; 16-byte aligned).
  *   importance  fp32 [cols] per-input-column weights, required for WMSE,
- *               ignored otherwise (may be NULL).
+ *               ignored otherwise (may be NULL); 16-byte aligned wherever it
+ *               is used (it is read four weights at a time), else
+ *               FP4Q_E_ALIGN.
  *   codes       [rows*cols/2] bytes, 8-byte aligned (16 for MXFP4).
  *   scales      [rows*cols/block] bytes.
  *   global_scale  one fp32: output (or input when global_scale_given); may be

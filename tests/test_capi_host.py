@@ -180,3 +180,11 @@ def test_noalloc_rejects_bad_arguments_before_any_hip_call(L):
     assert qn(spec(), gs=None) == -1
     assert qn(spec(scale_rule=1, objective=1)) == -1        # WMSE without importance
     assert L.fp4q_status_string(-7) != b"unknown status"
+
+
+def test_importance_must_be_16_byte_aligned_where_used(L):
+    # 4-byte aligned (an offset view of a weight vector): refused before any
+    # HIP call (only rejected calls are made here: the pointers are fake)
+    s = spec(scale_rule=1, objective=1)
+    assert q(L, s, imp=C.c_void_p(IMP.value + 4), dtype=B.FP4Q_F32) == -6
+    assert q(L, spec(format=2, objective=1), imp=C.c_void_p(IMP.value + 8)) == -6
