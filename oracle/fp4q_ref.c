@@ -197,6 +197,86 @@ float fp4q_ref_int4_step(void)
     return 6.0f / 7.0f;
 }
 
+/* ---- IF3 and IF6: the adaptive type at 3 and 6 bits ------------------ */
+/* [IF4, Methodology: the same idea applies to 3-bit (IF3) and 6-bit (IF6)
+ * formats].  The page names the types but fixes no grid, so the reading is
+ * the one under which n = 4 is exactly IF4: the FP element of an n-bit type
+ * is E2M(n-3) -- a sign bit, two exponent bits with bias 1 and n-3 mantissa
+ * bits, exponent field 0 subnormal, no infinities or NaN (E2M0, E2M1 and
+ * the OCP FP6 E2M3); the INT element is an integer in
+ * [-(2^(n-1) - 1), 2^(n-1) - 1]; an INT block uses the step
+ * D * fl32(FPmax / INTmax), which maps the INT maximum onto the FP maximum
+ * as 6/7 does for IF4; everything else is IF4's (E4M3 block scale with the
+ * indicator in bit 7, base scale E4M3(max|x| / (FPmax S)), and the global
+ * scale S = max|x| / (256 FPmax), 256*6 for FP4 [SS, Method 2]). */
+
+/* value of magnitude code m (0 .. 2^(n-1) - 1) of E2M(n-3) */
+float fp4q_ref_fpn_value(int n, int m)
+{
+    int k = n - 3;                 /* mantissa bits */
+    int e = (m >> k) & 3;
+    int f = m & ((1 << k) - 1);
+    double frac = ldexp((double)f, -k);
+    if (e == 0)
+        return (float)frac;        /* subnormal: f / 2^k */
+    return (float)ldexp(1.0 + frac, e - 1);
+}
+
+/* largest magnitude of E2M(n-3): 4, 6 and 7.5 for n = 3, 4, 6 */
+float fp4q_ref_fpn_max(int n)
+{
+    return fp4q_ref_fpn_value(n, (1 << (n - 1)) - 1);
+}
+
+/* nearest E2M(n-3) magnitude code to y >= 0, the even code on an exact tie,
+ * saturating at the largest magnitude */
+int fp4q_ref_fpn_round(int n, float y)
+{
+    int top = (1 << (n - 1)) - 1;
+    if (y >= fp4q_ref_fpn_max(n))
+        return top;
+    int best = 0;
+    double bestd = INFINITY;
+    for (int m = 0; m <= top; ++m) {
+        double d = fabs((double)y - (double)fp4q_ref_fpn_value(n, m));
+        if (d < bestd || (d == bestd && (m & 1) == 0 && (best & 1) == 1)) {
+            best = m;
+            bestd = d;
+        }
+    }
+    return best;
+}
+
+/* nearest integer in 0 .. 2^(n-1) - 1 to y >= 0, ties to even, saturating */
+int fp4q_ref_intn_round(int n, float y)
+{
+    int top = (1 << (n - 1)) - 1;
+    if (y >= (float)top)
+        return top;
+    int best = 0;
+    double bestd = INFINITY;
+    for (int q = 0; q <= top; ++q) {
+        double d = fabs((double)y - (double)q);
+        if (d < bestd || (d == bestd && (q & 1) == 0 && (best & 1) == 1)) {
+            best = q;
+            bestd = d;
+        }
+    }
+    return best;
+}
+
+/* the INT step factor fl32(FPmax / INTmax): 4/3, 6/7 and 7.5/31 */
+float fp4q_ref_ifn_step(int n)
+{
+    return fp4q_ref_fpn_max(n) / (float)((1 << (n - 1)) - 1);
+}
+
+/* bits per element of a format: 3 for IF3, 6 for IF6, 4 otherwise */
+static int format_bits(int format)
+{
+    return format == REF_IF3 ? 3 : (format == REF_IF6 ? 6 : 4);
+}
+
 /* ------------------------------------------------------------------------ */
 /* Hadamard and global scale                                                */
 /* ------------------------------------------------------------------------ */
@@ -234,6 +314,16 @@ float fp4q_ref_global_scale(float g)
     if (g == 0.0f)
         return 1.0f;
     float s = g / 1536.0f;
+    float floor_s = (float)ldexp(1.0, -117);
+    return s < floor_s ? floor_s : s;
+}
+
+/* the same rule for the n-bit adaptive types: S = max|x| / (256 FPmax) */
+float fp4q_ref_ifn_global_scale(int n, float g)
+{
+    if (g == 0.0f)
+        return 1.0f;
+    float s = g / (256.0f * fp4q_ref_fpn_max(n));
     float floor_s = (float)ldexp(1.0, -117);
     return s < floor_s ? floor_s : s;
 }
@@ -409,6 +499,62 @@ double fp4q_ref_int4_block(const float* xb, int B, const float* w, float S,
     return E;
 }
 
+/* base scale of an n-bit adaptive type: E4M3(max|x| / (FPmax S)), >= 1 */
+int fp4q_ref_ifn_base_scale(int n, const float* xb, int B, float S)
+{
+    float a = block_absmax(xb, B);
+    if (a == 0.0f)
+        return 0;
+    float sm = fp4q_ref_fpn_max(n) * S;
+    int sb = fp4q_ref_e4m3_round(a / sm);
+    return sb == 0 ? 1 : sb;
+}
+
+/* FP branch of an n-bit adaptive type with scale byte c: codes are
+ * sign << (n-1) | magnitude code */
+double fp4q_ref_fpn_block(int n, const float* xb, int B, const float* w, float S,
+                          int c, uint8_t* codes)
+{
+    float s = fp4q_ref_e4m3_value(c);
+    float D = s * S;
+    float r = 1.0f / D;
+    double E = 0.0;
+    for (int i = 0; i < B; ++i) {
+        float a = fabsf(xb[i]);
+        float y = a * r;
+        int m = fp4q_ref_fpn_round(n, y);
+        float xh = fp4q_ref_fpn_value(n, m) * D;
+        E = E + elem_err(a, xh, w, i);
+        if (codes)
+            codes[i] = (uint8_t)((signbit(xb[i]) ? (1 << (n - 1)) : 0) | m);
+    }
+    return E;
+}
+
+/* INT branch: step D * fl32(FPmax / INTmax); codes are the n-bit two's
+ * complement of the signed integer */
+double fp4q_ref_intn_block(int n, const float* xb, int B, const float* w, float S,
+                           int c, uint8_t* codes)
+{
+    float s = fp4q_ref_e4m3_value(c);
+    float D = s * S;
+    float Di = D * fp4q_ref_ifn_step(n);
+    float ri = 1.0f / Di;
+    double E = 0.0;
+    for (int i = 0; i < B; ++i) {
+        float a = fabsf(xb[i]);
+        float y = a * ri;
+        int q = fp4q_ref_intn_round(n, y);
+        float xh = (float)q * Di;
+        E = E + elem_err(a, xh, w, i);
+        if (codes) {
+            int sq = signbit(xb[i]) ? -q : q;
+            codes[i] = (uint8_t)(sq & ((1 << n) - 1));
+        }
+    }
+    return E;
+}
+
 typedef struct {
     const float* xb;
     int B;
@@ -469,6 +615,33 @@ static void put_nibbles(uint8_t* codes, int64_t elem0, const uint8_t* nib, int B
 {
     for (int i = 0; i < B; i += 2)
         codes[(elem0 + i) / 2] = (uint8_t)((nib[i] & 0xF) | ((nib[i + 1] & 0xF) << 4));
+}
+
+/* n-bit codes: element e of the tensor occupies bits n e .. n e + n - 1 of
+ * the code stream, least significant bit first (for n = 4: element 2k in the
+ * low nibble of byte k, as put_nibbles writes) */
+static void put_codes(uint8_t* codes, int64_t elem0, const uint8_t* c, int B, int n)
+{
+    for (int i = 0; i < B; ++i) {
+        for (int b = 0; b < n; ++b) {
+            int64_t bit = (elem0 + i) * n + b;
+            uint8_t mask = (uint8_t)(1u << (bit & 7));
+            if ((c[i] >> b) & 1)
+                codes[bit >> 3] |= mask;
+            else
+                codes[bit >> 3] &= (uint8_t)~mask;
+        }
+    }
+}
+
+static int get_code(const uint8_t* codes, int64_t e, int n)
+{
+    int v = 0;
+    for (int b = 0; b < n; ++b) {
+        int64_t bit = e * n + b;
+        v |= ((codes[bit >> 3] >> (bit & 7)) & 1) << b;
+    }
+    return v;
 }
 
 /* keep the first least error among candidates tried in order; also the
@@ -565,9 +738,30 @@ static void quant_rows(void* p, int64_t r0, int64_t r1)
                 /* all-zero block: scale byte 0, codes keep only the sign */
                 sbyte = 0;
                 for (int i = 0; i < B; ++i)
-                    nib[i] = (uint8_t)(signbit(xb[i]) ? 8 : 0);
+                    nib[i] = (uint8_t)(signbit(xb[i]) ? 1 << (format_bits(q->format) - 1) : 0);
                 best = 0.0;
-                second = (q->format == REF_IF4 || q->rule != REF_ABSMAX) ? 0.0 : INFINITY;
+                second = (q->format != REF_NVFP4 || q->rule != REF_ABSMAX) ? 0.0 : INFINITY;
+            } else if (q->format == REF_IF3 || q->format == REF_IF6) {
+                /* the n-bit adaptive type: per pattern the FP grid first, then
+                 * the INT grid (indicator bit 7), as IF4 */
+                int n = format_bits(q->format);
+                int sb = fp4q_ref_ifn_base_scale(n, xb, B, q->S);
+                int lo = q->rule == REF_SWEEP ? q->lo : 0;
+                int hi = q->rule == REF_SWEEP ? q->hi : 0;
+                int cprev = -1;
+                for (int k = lo; k <= hi; ++k) {
+                    int c = clamp_pattern(sb + k);
+                    if (c == cprev)
+                        continue;
+                    cprev = c;
+                    consider(fp4q_ref_fpn_block(n, xb, B, w, q->S, c, NULL), c, &best, &second, &cbest);
+                    consider(fp4q_ref_intn_block(n, xb, B, w, q->S, c, NULL), c | 0x80, &best, &second, &cbest);
+                }
+                if (cbest & 0x80)
+                    fp4q_ref_intn_block(n, xb, B, w, q->S, cbest & 0x7F, nib);
+                else
+                    fp4q_ref_fpn_block(n, xb, B, w, q->S, cbest, nib);
+                sbyte = (uint8_t)cbest;
             } else {
                 int sb = fp4q_ref_base_scale(xb, B, q->S);
                 if (q->format == REF_IF4) {
@@ -613,7 +807,10 @@ static void quant_rows(void* p, int64_t r0, int64_t r1)
                     fp4q_ref_nvfp4_block(xb, B, w, q->S, cbest, nib);
                 }
             }
-            put_nibbles(q->codes, e0, nib, B);
+            if (format_bits(q->format) == 4)
+                put_nibbles(q->codes, e0, nib, B);
+            else
+                put_codes(q->codes, e0, nib, B, format_bits(q->format));
             q->scales[bi] = sbyte;
             if (q->best)
                 q->best[bi] = best;
@@ -651,7 +848,7 @@ static int check_common(int format, int block, int rotate, int64_t rows, int64_t
     if (format == REF_MXFP4) {
         if (block != 32)
             return -4;
-    } else if (format == REF_NVFP4 || format == REF_IF4) {
+    } else if (format == REF_NVFP4 || format == REF_IF4 || format == REF_IF3 || format == REF_IF6) {
         if (block != 16)
             return -4;
     } else {
@@ -707,7 +904,9 @@ int fp4q_ref_quantize(int format, int block, int scale_rule, int objective,
                 if (rowmax[r] > g)
                     g = rowmax[r];
             free(rowmax);
-            S = fp4q_ref_global_scale(g);
+            S = (format == REF_IF3 || format == REF_IF6)
+                    ? fp4q_ref_ifn_global_scale(format_bits(format), g)
+                    : fp4q_ref_global_scale(g);
             *global_scale = S;
         }
     }
@@ -793,7 +992,7 @@ int fp4q_ref_quantize_relaxed(int format, int block, int global_scale_given,
     int rc = check_common(format, block, 0, rows, cols);
     if (rc)
         return rc;
-    if (format == REF_IF4)
+    if (format == REF_IF4 || format == REF_IF3 || format == REF_IF6)
         return -4;
     if (group != 8 && group != block)
         return -2;
@@ -839,6 +1038,17 @@ typedef struct {
 /* value of one stored element of block with scale byte sb */
 static float deq_elem(int format, int sb, int nibble, float S)
 {
+    if (format == REF_IF3 || format == REF_IF6) {
+        int n = format_bits(format);
+        float D = fp4q_ref_e4m3_value(sb & 0x7F) * S;
+        if (sb & 0x80) {
+            float Di = D * fp4q_ref_ifn_step(n);
+            int q = (nibble & (1 << (n - 1))) ? nibble - (1 << n) : nibble;
+            return (float)q * Di;
+        }
+        float v = fp4q_ref_fpn_value(n, nibble & ((1 << (n - 1)) - 1)) * D;
+        return (nibble >> (n - 1)) ? -v : v;
+    }
     if (format == REF_MXFP4) {
         float D = fp4q_ref_e8m0_value(sb);
         float v = fp4q_ref_e2m1_value(nibble & 7) * D;
@@ -868,7 +1078,8 @@ static void deq_rows(void* p, int64_t r0, int64_t r1)
             float* o = d->out + e0;
             for (int i = 0; i < B; ++i) {
                 int64_t e = e0 + i;
-                int nib = (e & 1) ? (d->codes[e / 2] >> 4) : (d->codes[e / 2] & 0xF);
+                int nib = format_bits(d->format) != 4 ? get_code(d->codes, e, format_bits(d->format))
+                        : (e & 1) ? (d->codes[e / 2] >> 4) : (d->codes[e / 2] & 0xF);
                 o[i] = deq_elem(d->format, sb, nib, d->S);
             }
             if (d->unrotate)

@@ -32,7 +32,7 @@ extern "C" {
 #endif
 
 /* numeric codes used by the oracle's own entry points */
-enum { REF_NVFP4 = 0, REF_MXFP4 = 1, REF_IF4 = 2 };
+enum { REF_NVFP4 = 0, REF_MXFP4 = 1, REF_IF4 = 2, REF_IF3 = 3, REF_IF6 = 4 };
 enum { REF_F32 = 0, REF_BF16 = 1 };
 enum { REF_ABSMAX = 0, REF_SWEEP = 1, REF_FOUR_SIX = 2 };
 enum { REF_MSE = 0, REF_WMSE = 1 };
@@ -47,6 +47,25 @@ int   fp4q_ref_int4_round(float y);        /* y >= 0 -> nearest integer 0..7  */
 float fp4q_ref_bf16_to_f32(uint16_t h);
 uint16_t fp4q_ref_f32_to_bf16(float f);    /* round to nearest even            */
 float fp4q_ref_int4_step(void);            /* fl32(6/7)                        */
+
+/* ---- IF3 / IF6: the adaptive type at n = 3 and 6 bits ------------------
+ * [IF4, Methodology: the idea applies to 3-bit (IF3) and 6-bit (IF6)
+ * formats].  Reading: FP element E2M(n-3) (bias 1, exponent field 0
+ * subnormal), INT element in [-(2^(n-1)-1), 2^(n-1)-1] with step
+ * D * fl32(FPmax/INTmax), E4M3 scale with the indicator in bit 7, base scale
+ * E4M3(max/(FPmax S)), S = max|x|/(256 FPmax); n = 4 is exactly IF4.  Codes
+ * are n-bit fields, element e at bits n*e .. n*e+n-1 of the code stream. */
+float fp4q_ref_fpn_value(int n, int m);    /* magnitude code -> value         */
+float fp4q_ref_fpn_max(int n);             /* 4, 6, 7.5 for n = 3, 4, 6       */
+int   fp4q_ref_fpn_round(int n, float y);  /* nearest code, even on tie, sat. */
+int   fp4q_ref_intn_round(int n, float y); /* nearest 0..2^(n-1)-1, even, sat.*/
+float fp4q_ref_ifn_step(int n);            /* fl32(FPmax / INTmax)            */
+float fp4q_ref_ifn_global_scale(int n, float g);
+int   fp4q_ref_ifn_base_scale(int n, const float* xb, int B, float S);
+double fp4q_ref_fpn_block(int n, const float* xb, int B, const float* w, float S,
+                          int c, uint8_t* codes);
+double fp4q_ref_intn_block(int n, const float* xb, int B, const float* w, float S,
+                           int c, uint8_t* codes);
 
 /* ---- transform and global scale --------------------------------------- */
 float fp4q_ref_rotation_scale(int n);      /* fl32(1/sqrt(n))                  */

@@ -10,7 +10,7 @@ import numpy as np
 
 from . import build as _build
 
-NVFP4, MXFP4, IF4 = 0, 1, 2
+NVFP4, MXFP4, IF4, IF3, IF6 = 0, 1, 2, 3, 4
 F32, BF16 = 0, 1
 ABSMAX, SWEEP, FOUR_SIX = 0, 1, 2
 MSE, WMSE = 0, 1
@@ -36,6 +36,15 @@ def lib():
             "fp4q_ref_bf16_to_f32": (f, [C.c_uint16]),
             "fp4q_ref_f32_to_bf16": (C.c_uint16, [f]),
             "fp4q_ref_int4_step": (f, []),
+            "fp4q_ref_fpn_value": (f, [i, i]),
+            "fp4q_ref_fpn_max": (f, [i]),
+            "fp4q_ref_fpn_round": (i, [i, f]),
+            "fp4q_ref_intn_round": (i, [i, f]),
+            "fp4q_ref_ifn_step": (f, [i]),
+            "fp4q_ref_ifn_global_scale": (f, [i, f]),
+            "fp4q_ref_ifn_base_scale": (i, [i, vp, i, f]),
+            "fp4q_ref_fpn_block": (d, [i, vp, i, vp, f, i, vp]),
+            "fp4q_ref_intn_block": (d, [i, vp, i, vp, f, i, vp]),
             "fp4q_ref_rotation_scale": (f, [i]),
             "fp4q_ref_fwht": (None, [vp, i]),
             "fp4q_ref_global_scale": (f, [f]),
@@ -74,6 +83,16 @@ def block_size(fmt):
     return 32 if fmt == MXFP4 else 16
 
 
+def code_bits(fmt):
+    """Bits per element code: 3 for IF3, 6 for IF6, 4 otherwise."""
+    return {IF3: 3, IF6: 6}.get(fmt, 4)
+
+
+def code_bytes(fmt, n):
+    """Bytes of the code stream of n elements."""
+    return n * code_bits(fmt) // 8
+
+
 def default_window(objective, fmt=NVFP4):
     if fmt == MXFP4:
         return (0, 1)
@@ -88,7 +107,7 @@ def quantize(x, fmt=NVFP4, rule=ABSMAX, objective=MSE, window=None, rotate=0,
     B = block_size(fmt)
     lo, hi = window if window is not None else default_window(objective, fmt)
     nb = rows * cols // B
-    codes = np.zeros(rows * cols // 2, np.uint8)
+    codes = np.zeros(code_bytes(fmt, rows * cols), np.uint8)
     scales = np.zeros(nb, np.uint8)
     gs = np.array([global_scale if global_scale is not None else 0.0], np.float32)
     imp = None if importance is None else np.ascontiguousarray(importance, np.float32)
@@ -203,6 +222,32 @@ def candidate_errors(blocks, S, w=None, nthreads=0):
     if rc != 0:
         raise ValueError(rc)
     return out
+
+
+def unpack_codes(codes, fmt):
+    """The n-bit element codes of a code stream (element e at bits
+    n e .. n e + n - 1, least significant bit first)."""
+    n = code_bits(fmt)
+    bits = np.unpackbits(np.asarray(codes, np.uint8), bitorder="little")
+    bits = bits[: bits.size // n * n].reshape(-1, n).astype(np.uint16)
+    return (bits << np.arange(n, dtype=np.uint16)).sum(axis=1).astype(np.uint8)
+
+
+def fpn_block(n, xb, S, c, w=None):
+    """Error and codes of the FP branch of an n-bit adaptive type."""
+    xb = np.ascontiguousarray(xb, np.float32)
+    codes = np.zeros(len(xb), np.uint8)
+    w = None if w is None else np.ascontiguousarray(w, np.float32)
+    e = lib().fp4q_ref_fpn_block(n, _p(xb), len(xb), _p(w), S, c, _p(codes))
+    return e, codes
+
+
+def intn_block(n, xb, S, c, w=None):
+    xb = np.ascontiguousarray(xb, np.float32)
+    codes = np.zeros(len(xb), np.uint8)
+    w = None if w is None else np.ascontiguousarray(w, np.float32)
+    e = lib().fp4q_ref_intn_block(n, _p(xb), len(xb), _p(w), S, c, _p(codes))
+    return e, codes
 
 
 def unpack_nibbles(codes):

@@ -265,3 +265,111 @@ def relaxed_block(xb, S, coefs, byte=None, fmt="nvfp4"):
             m = 7 if np.isinf(y) else nearest(Fr(float(y)), E2M1)
         nib.append((8 if np.signbit(x) else 0) | m)
     return byte, nib
+
+
+# ---- the n-bit adaptive types (IF3, IF6; n = 4 is IF4) ---------------------
+# The FP element of an n-bit type is E2M(n-3): sign, two exponent bits with
+# bias 1, n-3 mantissa bits, exponent field 0 subnormal; the INT element an
+# integer in [-(2^(n-1)-1), 2^(n-1)-1] with step D * fl32(FPmax/INTmax).
+
+def fpn_grid(n):
+    """The 2^(n-1) non-negative E2M(n-3) values, by magnitude code, from the
+    bit fields (exponent e = code >> (n-3), mantissa f = the low n-3 bits)."""
+    k = n - 3
+    vals = []
+    for code in range(1 << (n - 1)):
+        e, f = code >> k, code & ((1 << k) - 1)
+        frac = Fr(f, 1 << k)
+        vals.append(frac if e == 0 else (1 + frac) * Fr(2) ** (e - 1))
+    return vals
+
+
+def ifn_step(n):
+    grid = fpn_grid(n)
+    return f32(float(grid[-1])) / f32((1 << (n - 1)) - 1)
+
+
+def ifn_global_scale(n, g):
+    g = f32(g)
+    if g == 0:
+        return f32(1.0)
+    s = g / (f32(256.0) * f32(float(fpn_grid(n)[-1])))
+    return max(s, f32(2.0 ** -117))
+
+
+def ifn_base_byte(n, a, S):
+    t = f32(a) / (f32(float(fpn_grid(n)[-1])) * f32(S))
+    return max(nearest(Fr(float(t)), E4M3), 1)
+
+
+def encode_fpn(n, xb, S, c, w=None):
+    """(exact error, codes) of the FP branch with scale byte c."""
+    grid = fpn_grid(n)
+    S = f32(S)
+    D = f32(float(E4M3[c])) * S
+    r = f32(1.0) / D
+    err, codes = Fr(0), []
+    for i, x in enumerate(xb):
+        x = f32(x)
+        a = abs(x)
+        y = a * r
+        m = nearest(Fr(float(y)), grid)
+        xh = f32(float(grid[m])) * D
+        e = (Fr(float(a)) - Fr(float(xh))) ** 2
+        if w is not None:
+            e *= Fr(float(f32(w[i])))
+        err += e
+        codes.append(((1 << (n - 1)) if np.signbit(x) else 0) | m)
+    return err, codes
+
+
+def encode_intn(n, xb, S, c, w=None):
+    top = (1 << (n - 1)) - 1
+    S = f32(S)
+    D = f32(float(E4M3[c])) * S
+    Di = D * ifn_step(n)
+    ri = f32(1.0) / Di
+    err, codes = Fr(0), []
+    for i, x in enumerate(xb):
+        x = f32(x)
+        a = abs(x)
+        y = a * ri
+        q = nearest(Fr(float(y)), [Fr(k) for k in range(top + 1)])
+        xh = f32(q) * Di
+        e = (Fr(float(a)) - Fr(float(xh))) ** 2
+        if w is not None:
+            e *= Fr(float(f32(w[i])))
+        err += e
+        codes.append((-q if np.signbit(x) else q) & ((1 << n) - 1))
+    return err, codes
+
+
+def quantize_block_ifn(n, xb, S, window=(0, 0), w=None):
+    """(scale byte, codes, exact error): per pattern of the window the FP
+    grid, then the INT grid; the first least error wins."""
+    a = max(abs(f32(v)) for v in xb)
+    if a == 0:
+        return 0, [((1 << (n - 1)) if np.signbit(f32(v)) else 0) for v in xb], Fr(0)
+    sb = ifn_base_byte(n, a, S)
+    opts, seen = [], set()
+    for k in range(window[0], window[1] + 1):
+        c = min(0x7E, max(0x01, sb + k))
+        if c in seen:
+            continue
+        seen.add(c)
+        ef, cf = encode_fpn(n, xb, S, c, w)
+        ei, ci = encode_intn(n, xb, S, c, w)
+        opts.append((ef, 2 * len(opts), c, cf))
+        opts.append((ei, 2 * len(opts) + 1, c | 0x80, ci))
+    e, _, byte, codes = min(opts, key=lambda o: (o[0], o[1]))
+    return byte, codes, e
+
+
+def pack_bits(codes, n):
+    """Code stream of n-bit codes: code i at bits n i .. n i + n - 1, least
+    significant bit first."""
+    total = 0
+    for i, c in enumerate(codes):
+        total |= (int(c) & ((1 << n) - 1)) << (n * i)
+    nbytes = (len(codes) * n + 7) // 8
+    return bytes((total >> (8 * b)) & 0xFF for b in range(nbytes))
