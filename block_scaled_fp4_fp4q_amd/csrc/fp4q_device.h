@@ -115,6 +115,18 @@ __device__ __forceinline__ void fp4_unpack2_scaled(uint32_t packed, float& a, fl
     b = t[1];
 }
 
+// A register of unspecified value, to start a packed code word whose four
+// bytes the following conversions all overwrite.  The empty asm emits
+// nothing; taking `tie` as an input keeps each use a statement of its own, so
+// that the compiler neither merges two of them (a conversion would then copy
+// the shared register first) nor has to materialize a constant.
+__device__ __forceinline__ uint32_t fresh_word(float tie)
+{
+    uint32_t w;
+    asm("" : "=v"(w) : "v"(tie));
+    return w;
+}
+
 // the 16 sign|magnitude nibbles of E2M1(v[i] * r), element 2k in the low
 // nibble of byte k
 __device__ __forceinline__ uint2 fp4_encode16(const float* v, float r)

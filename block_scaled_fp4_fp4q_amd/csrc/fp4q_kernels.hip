@@ -449,12 +449,14 @@ __global__ __launch_bounds__(kThreads) void nvfp4_absmax(
 // power-of-two scale 2 exactly, so one multiply serves both candidates.
 // With weights, b holds sqrt(w) and each term is formed as (b y - b q)^2, so
 // that the product b y serves both candidates of a pair as well.
-// The code words cw[] are scratch that every call overwrites completely;
-// carrying them from one candidate to the next lets each conversion reuse the
-// previous candidate's dead word instead of copying a fresh one.
+// Every code word starts from a fresh register of unspecified value (all four
+// bytes are written): a word handed on from the previous candidate would tie
+// each candidate's conversions to the end of the previous one's decodes.
+// With `words`, the first candidate's two code words (its 16 nibbles, the
+// method's codes) are stored there.
 template <bool WMSE, bool PAIR>
 __device__ __forceinline__ void fp4_err32(const float* v, const float* b, float r, float& F1, float& F2,
-                                          uint32_t (&cw)[4])
+                                          uint32_t* words = nullptr)
 {
     F1 = 0.0f;
     F2 = 0.0f;
@@ -464,7 +466,7 @@ __device__ __forceinline__ void fp4_err32(const float* v, const float* b, float 
 #pragma unroll
         for (int j = 0; j < 8; ++j)
             y[j] = v[8 * g + j] * r;
-        uint32_t c = cw[g], c2 = cw[2 + g];
+        uint32_t c = fresh_word(y[0]), c2 = fresh_word(y[1]);
         c = fp4_pack2<0>(c, y[0], y[1]);
         c = fp4_pack2<1>(c, y[2], y[3]);
         c = fp4_pack2<2>(c, y[4], y[5]);
@@ -483,8 +485,8 @@ __device__ __forceinline__ void fp4_err32(const float* v, const float* b, float 
             fp4_unpack2_scaled<2>(c2, h[4], h[5], 2.0f);
             fp4_unpack2_scaled<3>(c2, h[6], h[7], 2.0f);
         }
-        cw[g] = c;
-        cw[2 + g] = c2;
+        if (words)
+            words[g] = c;
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
             if constexpr (WMSE) {
@@ -543,10 +545,6 @@ __device__ __forceinline__ void sweep_fixed(const float* v, const float* b, cons
                                             uint32_t& p1, uint32_t& p2)
 {
     static_assert(HI - LO < 16, "the window offset must fit in four bits");
-    uint32_t cw[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-        cw[i] = __builtin_nondeterministic_value(0u);
 #pragma unroll
     for (int k = LO; k <= HI; ++k) {
         if (((k - LO) & 15) >= 8)
@@ -554,11 +552,11 @@ __device__ __forceinline__ void sweep_fixed(const float* v, const float* b, cons
         const float4 t = tab[sb + k];
         float F1, F2;
         if (k + 8 <= HI) {
-            fp4_err32<WMSE, true>(v, b, t.y, F1, F2, cw);
+            fp4_err32<WMSE, true>(v, b, t.y, F1, F2);
             keep_best_packed(F1 * t.z, (uint32_t)(k - LO), p1, p2);
             keep_best_packed(F2 * t.z, (uint32_t)(k + 8 - LO), p1, p2);
         } else {
-            fp4_err32<WMSE, false>(v, b, t.y, F1, F2, cw);
+            fp4_err32<WMSE, false>(v, b, t.y, F1, F2);
             keep_best_packed(F1 * t.z, (uint32_t)(k - LO), p1, p2);
         }
     }
@@ -730,7 +728,6 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
                     cb = (int)sb + FLO + (int)(p1 & 0xFu);
                     rel = 64.0f * u; // + 30u from the packed offsets
                 } else {
-                    uint32_t cw[4] = {0u, 0u, 0u, 0u};
                     // offsets k and k+8 pair up in runs of eight; the rest are singles
                     for (int k = lo; k <= hi; ++k) {
                         if (((k - lo) & 15) >= 8)
@@ -744,19 +741,19 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
                             float F1, F2, E2;
                             if (__builtin_amdgcn_ballot_w64(t.w == 0.0f) == 0) {
                                 // every lane's pair is an exact doubling: shared product
-                                fp4_err32<WMSE, true>(v, b, t.y, F1, F2, cw);
+                                fp4_err32<WMSE, true>(v, b, t.y, F1, F2);
                                 E2 = F2 * t.z;
                             } else {
                                 float unused;
-                                fp4_err32<WMSE, false>(v, b, t.y, F1, unused, cw);
-                                fp4_err32<WMSE, false>(v, b, tab[c8].y, F2, unused, cw);
+                                fp4_err32<WMSE, false>(v, b, t.y, F1, unused);
+                                fp4_err32<WMSE, false>(v, b, tab[c8].y, F2, unused);
                                 E2 = F2 * tab[c8].z;
                             }
                             keep_best(ok1 ? F1 * t.z : __builtin_huge_valf(), c, e1, e2, cb);
                             keep_best(ok2 ? E2 : __builtin_huge_valf(), c8, e1, e2, cb);
                         } else {
                             float F1, unused;
-                            fp4_err32<WMSE, false>(v, b, t.y, F1, unused, cw);
+                            fp4_err32<WMSE, false>(v, b, t.y, F1, unused);
                             keep_best(ok1 ? F1 * t.z : __builtin_huge_valf(), c, e1, e2, cb);
                         }
                     }
@@ -871,7 +868,7 @@ __global__ __launch_bounds__(kThreads) void if4_quant(
                 block_roots<16>(imp, root, wsum, roots_in_lds, col0, b, W);
             // the estimates also produce both candidates' codes: the FP4
             // conversion words (of y = v r, as the encode) and the INT4 nibbles
-            uint32_t cw[4] = {0u, 0u, 0u, 0u};
+            uint32_t cw[2];
             float Ff, unused;
             fp4_err32<WMSE, false>(v, b, r, Ff, unused, cw);
             uint2 int4_words;
@@ -1296,7 +1293,7 @@ __global__ __launch_bounds__(kThreads) void nvfp4_foursix(
                 if constexpr (WMSE)
                     block_roots<16>(imp, root, wsum, roots_in_lds, col0, b, W);
                 // the estimates' conversion words are each candidate's codes
-                uint32_t cw[4] = {0u, 0u, 0u, 0u};
+                uint32_t cw[2];
                 float F6, F4, unused;
                 fp4_err32<WMSE, false>(v, b, r6, F6, unused, cw);
                 const uint2 codes6 = make_uint2(cw[0], cw[1]);
@@ -1380,7 +1377,6 @@ __global__ __launch_bounds__(kThreads) void if4_sweep(
             float W = 16.0f;
             if constexpr (WMSE)
                 block_roots<16>(imp, root, wsum, roots_in_lds, col0, b, W);
-            uint32_t cw[4] = {0u, 0u, 0u, 0u};
             float e1 = __builtin_huge_valf(), e2 = __builtin_huge_valf();
             int cb = (int)sb, cprev = -1;
             for (int k = lo; k <= hi; ++k) {
@@ -1391,7 +1387,7 @@ __global__ __launch_bounds__(kThreads) void if4_sweep(
                 const float4 t = tab[c];
                 const float2 t2 = tab2[c];
                 float Ff, unused;
-                fp4_err32<WMSE, false>(v, b, t.y, Ff, unused, cw);
+                fp4_err32<WMSE, false>(v, b, t.y, Ff, unused);
                 keep_best(Ff * t2.x, c, e1, e2, cb);
                 keep_best(int4_est16<WMSE>(v, b, t.w) * t2.y, c | 0x80, e1, e2, cb);
             }
