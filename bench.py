@@ -29,7 +29,7 @@ separately) and the NVFP4 ScaleSweep WMSE [-8, 7] weight workload (bf16
 `configs` times the other workloads with their own rules (c1 NVFP4 AbsMax and
 ScaleSweep MSE, c3 MXFP4 with and without a 32-point Hadamard, c4 IF4);
 `extensions` times Four Over Six, the MXFP4 exponent window, the IF4 pattern
-window and the FOCUS deploy encode.  Every timed workload carries a
+window, IF6 and IF3 on the IF4 workload and the FOCUS deploy encode.  Every timed workload carries a
 `parity_sample` of its leading rows.  A plain 1 GiB device copy is the
 achievable-bandwidth yardstick.
 """
@@ -255,7 +255,7 @@ def sample_parity(x_h, spec, codes, scales, gs, importance=None, relaxed=None):
                             global_scale=S, importance=importance, nthreads=cores, errors=True)
     nb = r * cols // spec.block
     got_s = scales.cpu().numpy()[:nb]
-    got_c = codes.cpu().numpy()[: r * cols // 2]
+    got_c = codes.cpu().numpy()[: ref.code_bytes(spec.format, r * cols)]
     out = {"rows": r, "blocks": nb, "scale_mismatches": int(np.sum(got_s != want["scales"])),
            "code_bytes_mismatched": int(np.sum(got_c != want["codes"]))}
     if "best" in want:
@@ -279,7 +279,7 @@ def extensions(args, B, synth, dev, x2, imp, ws, x2_h, imp_h):
             bytes_per_elem=None, base_rotate=None, x_h=None, imp_host=None):
         rows, cols = x.shape
         n = rows * cols
-        codes = torch.empty(n // 2, dtype=torch.uint8, device=dev)
+        codes = torch.empty(B.code_bytes(spec.format, n), dtype=torch.uint8, device=dev)
         scales = torch.empty(n // spec.block, dtype=torch.uint8, device=dev)
         gs = torch.empty(1, dtype=torch.float32, device=dev)
         # enough copies (>= 512 MiB) that no step finds its input in the Infinity Cache
@@ -295,7 +295,7 @@ def extensions(args, B, synth, dev, x2, imp, ws, x2_h, imp_h):
         espec = B.make_spec(spec.format, rotate=rotate)
         e = B.fp4q_error(espec, x, err_imp, codes, scales, gs, ws)
         base_rot = rotate if base_rotate is None else base_rotate
-        bcodes = torch.empty(n // 2, dtype=torch.uint8, device=dev)
+        bcodes = torch.empty(B.code_bytes(base_spec.format, n), dtype=torch.uint8, device=dev)
         bscales = torch.empty(n // base_spec.block, dtype=torch.uint8, device=dev)
         B.fp4q_quantize(base_spec, x, importance, bcodes, bscales, gs, ws)
         eb = B.fp4q_error(B.make_spec(base_spec.format, rotate=base_rot), x, err_imp, bcodes, bscales,
@@ -378,6 +378,11 @@ def extensions(args, B, synth, dev, x2, imp, ws, x2_h, imp_h):
         f"parity {out['mxfp4_focus_deploy_g8_c3'].get('parity_sample')}")
     del x3, c, r3, s3
 
+    for name, fmt, bits in (("if6_c4", B.FP4Q_IF6, 6), ("if3_c4", B.FP4Q_IF3, 3)):
+        run(name, f"{name[:3].upper()} (FP{bits} or INT{bits} per block, indicator in the scale's "
+            "sign bit), bf16 8192x8192 half uniform / half spiky-Laplace blocks; baseline IF4",
+            x4, B.make_spec(fmt), base_spec=B.make_spec(B.FP4Q_IF4),
+            bytes_per_elem=2 * 2.0 + bits / 8 + 1.0 / 16, x_h=x4_h)
     run("if4_pattern_window_c4",
         "IF4 (FP4 or INT4 per block) over E4M3 patterns [-3,7], MSE, bf16 8192x8192 "
         "half uniform / half spiky-Laplace blocks; baseline plain IF4",

@@ -13,7 +13,7 @@ import torch
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libfp4q.so")
 
-FP4Q_NVFP4, FP4Q_MXFP4, FP4Q_IF4 = 0, 1, 2
+FP4Q_NVFP4, FP4Q_MXFP4, FP4Q_IF4, FP4Q_IF3, FP4Q_IF6 = 0, 1, 2, 3, 4
 FP4Q_F32, FP4Q_BF16 = 0, 1
 FP4Q_SCALE_ABSMAX, FP4Q_SCALE_SWEEP, FP4Q_SCALE_FOUR_OVER_SIX = 0, 1, 2
 FP4Q_OBJ_MSE, FP4Q_OBJ_WMSE = 0, 1
@@ -163,14 +163,23 @@ _F32 = (torch.float32,)
 _X = (torch.float32, torch.bfloat16)
 
 
+ADAPTIVE = (FP4Q_IF4, FP4Q_IF3, FP4Q_IF6)
+
+
+def code_bytes(format, n):
+    """Bytes of the code stream of n elements: n-bit codes for IF3 (3) and
+    IF6 (6), 4-bit codes otherwise."""
+    return n * {FP4Q_IF3: 3, FP4Q_IF6: 6}.get(format, 4) // 8
+
+
 def _needs_importance(spec):
     return spec.objective == FP4Q_OBJ_WMSE and (spec.scale_rule != FP4Q_SCALE_ABSMAX
-                                                or spec.format == FP4Q_IF4)
+                                                or spec.format in ADAPTIVE)
 
 
 def _check_outputs(spec, rows, cols, codes, scales, global_scale, dev, require_cuda):
     n = rows * cols
-    _check_tensor("codes", codes, _U8, n // 2, dev, require_cuda)
+    _check_tensor("codes", codes, _U8, code_bytes(spec.format, n), dev, require_cuda)
     _check_tensor("scales", scales, _U8, n // spec.block, dev, require_cuda)
     _check_tensor("global_scale", global_scale, _F32, 1, dev, require_cuda,
                   optional=spec.format == FP4Q_MXFP4)
@@ -323,13 +332,13 @@ def alloc_workspace(spec, rows, cols, device):
 def quantize(x, format=FP4Q_NVFP4, scale_rule=FP4Q_SCALE_ABSMAX, objective=FP4Q_OBJ_MSE,
              window=None, rotate=0, importance=None, global_scale=None, workspace=None,
              stream=None):
-    """Returns (codes uint8 [rows*cols/2], scales uint8 [rows*cols/block],
-    global_scale float32 [1])."""
+    """Returns (codes uint8 [code_bytes(format, rows*cols)], scales uint8
+    [rows*cols/block], global_scale float32 [1])."""
     spec = make_spec(format, scale_rule, objective, window, rotate, global_scale is not None)
     x2 = _as_2d(x)
     rows, cols = x2.shape
     dev = x.device
-    codes = torch.empty(rows * cols // 2, dtype=torch.uint8, device=dev)
+    codes = torch.empty(code_bytes(format, rows * cols), dtype=torch.uint8, device=dev)
     scales = torch.empty(rows * cols // spec.block, dtype=torch.uint8, device=dev)
     if global_scale is None:
         gs = torch.empty(1, dtype=torch.float32, device=dev)

@@ -16,12 +16,30 @@ bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p
 
 int block_of(int32_t format) { return format == FP4Q_MXFP4 ? 32 : 16; }
 
+bool is_adaptive(int32_t format)
+{
+    return format == FP4Q_IF4 || format == FP4Q_IF3 || format == FP4Q_IF6;
+}
+
+// alignment of the codes pointer: one block's codes are read and written as
+// 8 (NVFP4, IF4), 16 (MXFP4), 12 (IF6, as 32-bit words) or 6 bytes (IF3, as
+// 16-bit halves)
+uintptr_t codes_align(int32_t format)
+{
+    switch (format) {
+    case FP4Q_MXFP4: return 16;
+    case FP4Q_IF6: return 4;
+    case FP4Q_IF3: return 2;
+    default: return 8;
+    }
+}
+
 // common checks of a spec; the window is only meaningful for SWEEP
 fp4q_status check_spec(const fp4q_spec* s, bool for_quantize)
 {
     if (!s)
         return FP4Q_E_NULL;
-    if (s->format != FP4Q_NVFP4 && s->format != FP4Q_MXFP4 && s->format != FP4Q_IF4)
+    if (s->format != FP4Q_NVFP4 && s->format != FP4Q_MXFP4 && !is_adaptive(s->format))
         return FP4Q_E_ARG;
     if (s->block != block_of(s->format))
         return FP4Q_E_UNSUPPORTED;
@@ -73,12 +91,12 @@ fp4q_status check_quantize(const fp4q_spec* spec, const void* x, int32_t x_dtype
     const bool has_gs = spec->format != FP4Q_MXFP4;
     // the weights matter wherever a block error decides between candidates
     const bool wants_imp = spec->objective == FP4Q_OBJ_WMSE &&
-                           (spec->scale_rule != FP4Q_SCALE_ABSMAX || spec->format == FP4Q_IF4);
+                           (spec->scale_rule != FP4Q_SCALE_ABSMAX || is_adaptive(spec->format));
     const bool empty = rows == 0 || cols == 0; // tensor pointers may then be NULL
     if ((!empty && (!x || !codes || !scales)) || (has_gs && !global_scale) ||
         (wants_imp && !empty && !importance))
         return FP4Q_E_NULL;
-    if (!aligned(x, 16) || !aligned(codes, spec->block == 32 ? 16 : 8) ||
+    if (!aligned(x, 16) || !aligned(codes, codes_align(spec->format)) ||
         (wants_imp && !aligned(importance, 16)) || (has_gs && !aligned(global_scale, 4)))
         return FP4Q_E_ALIGN;
     a.format = spec->format;
@@ -113,7 +131,7 @@ const char* fp4q_status_string(fp4q_status s)
     case FP4Q_E_NULL: return "a required pointer is NULL";
     case FP4Q_E_ARG: return "invalid argument (enum, window, rotation or workspace size)";
     case FP4Q_E_SHAPE: return "invalid shape (negative size, or cols not a multiple of the block)";
-    case FP4Q_E_UNSUPPORTED: return "unsupported combination (block size, Four Over Six outside NVFP4, relaxed IF4 or rotation)";
+    case FP4Q_E_UNSUPPORTED: return "unsupported combination (block size, Four Over Six outside NVFP4, relaxed encode of IF3/IF4/IF6 or with rotation)";
     case FP4Q_E_HIP: return "the HIP runtime refused a launch or copy";
     case FP4Q_E_ALIGN: return "a tensor pointer is not aligned as required";
     case FP4Q_E_SCRATCH: return "the problem needs more scratch than fp4q_quantize_noalloc holds";
@@ -176,7 +194,7 @@ fp4q_status fp4q_quantize_relaxed(const fp4q_spec* spec, const void* x, int32_t 
         return st;
     if ((st = check_shape(rows, cols, spec->block)) != FP4Q_OK)
         return st;
-    if (spec->format == FP4Q_IF4 || spec->rotate != 0)
+    if (is_adaptive(spec->format) || spec->rotate != 0)
         return FP4Q_E_UNSUPPORTED;
     if (!valid_dtype(x_dtype) || (coef_group != 8 && coef_group != spec->block) ||
         (scales_given != 0 && scales_given != 1) ||
@@ -224,7 +242,7 @@ fp4q_status fp4q_dequantize(const fp4q_spec* spec, const uint8_t* codes, const u
     const bool empty = rows == 0 || cols == 0;
     if ((!empty && (!codes || !scales || !y)) || (has_gs && !empty && !global_scale))
         return FP4Q_E_NULL;
-    if (!aligned(codes, spec->block == 32 ? 16 : 8) || !aligned(y, 16) ||
+    if (!aligned(codes, codes_align(spec->format)) || !aligned(y, 16) ||
         (has_gs && !aligned(global_scale, 4)))
         return FP4Q_E_ALIGN;
     fp4q::DequantArgs a{};
@@ -259,7 +277,7 @@ fp4q_status fp4q_error(const fp4q_spec* spec, const void* x, int32_t x_dtype, in
         return FP4Q_E_NULL;
     if (ws_bytes < fp4q::kWorkspaceBytes)
         return FP4Q_E_ARG;
-    if (!aligned(x, 16) || !aligned(codes, spec->block == 32 ? 16 : 8) || !aligned(workspace, 256) ||
+    if (!aligned(x, 16) || !aligned(codes, codes_align(spec->format)) || !aligned(workspace, 256) ||
         (has_gs && !aligned(global_scale, 4)) || !aligned(importance, 4))
         return FP4Q_E_ALIGN;
     fp4q::ErrorArgs a{};

@@ -1579,15 +1579,285 @@ __global__ __launch_bounds__(kThreads) void relaxed_quant_lanes(
 }
 
 // ---------------------------------------------------------------------------
+// IF3 / IF6: the adaptive FP-or-INT type at 3 and 6 bits
+//
+// Adaptive Block-Scaled Data Types, Methodology: the per-block pick between
+// an FP grid and a scaled INT grid applies to 3- and 6-bit types as well.
+// The n-bit type here is the one whose n = 4 case is IF4: FP element E2M(n-3)
+// (E2M0 magnitudes {0, 1, 2, 4}; OCP E2M3, 1/8 steps below 2, 1/4 below 4,
+// 1/2 up to 7.5), INT element in [-(2^(n-1)-1), 2^(n-1)-1] with step
+// D fl32(FPmax/INTmax), E4M3 block scale with the indicator in bit 7, base
+// scale E4M3(max|x| / (FPmax S)) and S = max|x| / (256 FPmax).  Codes are
+// n-bit fields, element e at bits n e .. n e + n - 1, least significant bit
+// first (IF6: 12 bytes per block, IF3: 6).  With two candidates per pattern
+// the block errors are evaluated in binary64 directly, in the method's order
+// of operations, so each pick equals the method's.
+// ---------------------------------------------------------------------------
+
+template <int N>
+struct IfnFormat {
+    static constexpr int kTop = (1 << (N - 1)) - 1;                 // INT maximum
+    static constexpr float kFpMax = N == 6 ? 7.5f : 4.0f;           // FP maximum
+    static constexpr float kScaleDen = 256.0f * kFpMax;             // S = G / (256 FPmax)
+    static constexpr int kWords = N == 6 ? 3 : 2;                   // 32-bit words per block's codes
+};
+
+// fl32(FPmax / INTmax): fl32(7.5/31) and fl32(4/3)
+template <int N>
+__device__ __forceinline__ float ifn_step() { return IfnFormat<N>::kFpMax / (float)IfnFormat<N>::kTop; }
+
+// nearest FP magnitude to y >= 0 (ties to the even code, saturating at the
+// largest); returns the value and sets its magnitude code
+template <int N>
+__device__ __forceinline__ float fpn_round(float y, uint32_t& code)
+{
+    if constexpr (N == 6) {
+        // adding 2^20 / 2^21 / 2^22 makes the binary32 ulp equal to the E2M3
+        // step of [0,2) / [2,4) / [4,inf): round-to-nearest-even does the rest
+        const float M = y < 2.0f ? 0x1p20f : (y < 4.0f ? 0x1p21f : 0x1p22f);
+        const float q = __builtin_fminf((y + M) - M, 7.5f);
+        const uint32_t u = __float_as_uint(q);
+        // subnormal codes 0..7 are 8 q; above, (exponent field + 1) << 3 | mantissa
+        code = q < 1.0f ? (uint32_t)(q * 8.0f) : ((((u >> 23) - 126u) << 3) | ((u >> 20) & 7u));
+        return q;
+    } else {
+        // E2M0 {0, 1, 2, 4}: the midpoints 0.5, 1.5 and 3 go to the even codes 0, 2, 2
+        code = y <= 0.5f ? 0u : (y < 1.5f ? 1u : (y <= 3.0f ? 2u : 3u));
+        return code == 3u ? 4.0f : (float)code;
+    }
+}
+
+// binary64 block error of the FP grid with step D, reciprocal r; with codes,
+// also the block's sign|magnitude codes
+template <int N, bool WMSE>
+__device__ __forceinline__ double fpn_error16(const float* v, const float* w, float D, float r,
+                                             uint32_t* codes)
+{
+    double E = 0.0;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        const float a = __builtin_fabsf(v[i]);
+        uint32_t m;
+        const float xh = fpn_round<N>(a * r, m) * D;
+        const double d = (double)a - (double)xh;
+        double t = d * d;
+        if constexpr (WMSE)
+            t = (double)w[i] * t;
+        E = E + t;
+        if (codes)
+            codes[i] = ((__float_as_uint(v[i]) >> 31) << (N - 1)) | m;
+    }
+    return E;
+}
+
+// the same for the INT grid with step Di, reciprocal ri: q = min(RNE(|x| ri),
+// INTmax); codes are the n-bit two's complement of +-q.  A zero element has
+// q = 0 (|x| / D_int = 0), also where D_int < 2^-128 makes ri infinite and
+// |x| ri would be NaN (IF6's step 7.5/31 is below 1/4, so that happens for
+// the smallest patterns under the smallest global scales).
+template <int N, bool WMSE>
+__device__ __forceinline__ double intn_error16(const float* v, const float* w, float Di, float ri,
+                                              uint32_t* codes)
+{
+    double E = 0.0;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        const float a = __builtin_fabsf(v[i]);
+        const float q = a == 0.0f ? 0.0f
+                                  : __builtin_fminf(__builtin_rintf(a * ri), (float)IfnFormat<N>::kTop);
+        const float xh = q * Di;
+        const double d = (double)a - (double)xh;
+        double t = d * d;
+        if constexpr (WMSE)
+            t = (double)w[i] * t;
+        E = E + t;
+        if (codes) {
+            const int sq = (__float_as_uint(v[i]) >> 31) ? -(int)q : (int)q;
+            codes[i] = (uint32_t)sq & ((1u << N) - 1u);
+        }
+    }
+    return E;
+}
+
+// the block's 16 n-bit codes as 32-bit words, code i at bits n i .. n i + n - 1
+template <int N>
+__device__ __forceinline__ void pack_ifn(const uint32_t* c, uint32_t* w)
+{
+    uint64_t lo = 0, hi = 0;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        const int sh = N * i;
+        if (sh < 64) {
+            lo |= (uint64_t)c[i] << sh;
+            if (sh + N > 64)
+                hi |= (uint64_t)c[i] >> (64 - sh);
+        } else {
+            hi |= (uint64_t)c[i] << (sh - 64);
+        }
+    }
+    w[0] = (uint32_t)lo;
+    w[1] = (uint32_t)(lo >> 32);
+    if constexpr (N == 6)
+        w[2] = (uint32_t)hi;
+}
+
+template <int N>
+__device__ __forceinline__ void store_ifn(uint8_t* __restrict__ codes, int64_t blk, const uint32_t* w)
+{
+    if constexpr (N == 6) { // 12 bytes, 4-byte aligned
+        uint32_t* p = reinterpret_cast<uint32_t*>(codes) + 3 * blk;
+        p[0] = w[0];
+        p[1] = w[1];
+        p[2] = w[2];
+    } else {                // 6 bytes, 2-byte aligned
+        uint16_t* p = reinterpret_cast<uint16_t*>(codes) + 3 * blk;
+        p[0] = (uint16_t)w[0];
+        p[1] = (uint16_t)(w[0] >> 16);
+        p[2] = (uint16_t)w[1];
+    }
+}
+
+// One lane per block.  Patterns of the window (one for the base scale alone)
+// are tried in ascending order, each with the FP grid and then the INT grid;
+// the first least binary64 error wins.
+template <int N, bool BF16, bool ROT, bool WMSE>
+__global__ __launch_bounds__(kThreads) void ifn_quant(
+    const void* __restrict__ x, int64_t nblocks, int64_t blocks_per_row,
+    const float* __restrict__ imp, const float* __restrict__ partials, int npart,
+    float* __restrict__ Sp, int lo, int hi, uint8_t* __restrict__ codes, uint8_t* __restrict__ scales)
+{
+    using F = IfnFormat<N>;
+    // per pattern: D = fl32(s S), r = fl32(1/D), D_int = fl32(D step), r_int
+    __shared__ float4 tab[128];
+    float S;
+    if (npart == 0) {
+        S = *Sp;
+    } else { // S = G / (256 FPmax), floored at 2^-117 (1 for G == 0)
+        __shared__ float red[kThreads / 64];
+        float m = 0.0f;
+        for (int i = threadIdx.x; i < npart; i += kThreads)
+            m = __builtin_fmaxf(m, partials[i]);
+        m = wave_max(m);
+        if ((threadIdx.x & 63) == 0)
+            red[threadIdx.x >> 6] = m;
+        __syncthreads();
+        float g = red[0];
+#pragma unroll
+        for (int w = 1; w < kThreads / 64; ++w)
+            g = __builtin_fmaxf(g, red[w]);
+        float s = g / F::kScaleDen;
+        s = __builtin_fmaxf(s, 0x1p-117f);
+        S = (g == 0.0f) ? 1.0f : s;
+        if (blockIdx.x == 0 && threadIdx.x == 0)
+            *Sp = S;
+    }
+    const float step = ifn_step<N>();
+    for (int c = threadIdx.x; c < 128; c += kThreads) {
+        const float D = e4m3_value((uint32_t)(c < 0x7E ? c : 0x7E)) * S;
+        const float Di = D * step;
+        tab[c] = make_float4(D, 1.0f / D, Di, 1.0f / Di);
+    }
+    __syncthreads();
+    const float SM = F::kFpMax * S;
+    for (int64_t blk = (int64_t)blockIdx.x * kThreads + threadIdx.x; blk < nblocks;
+         blk += (int64_t)gridDim.x * kThreads) {
+        float v[16];
+        load_block<16, BF16>(x, blk, v);
+        if constexpr (ROT)
+            fwht<16>(v);
+        const float a = block_absmax<16>(v);
+        uint32_t cds[16], words[F::kWords];
+        uint32_t sbyte = 0;
+        if (a == 0.0f) { // scale 0, codes keep only the signs
+#pragma unroll
+            for (int i = 0; i < 16; ++i)
+                cds[i] = (__float_as_uint(v[i]) >> 31) << (N - 1);
+        } else {
+            float w[16];
+            if constexpr (WMSE)
+                load_weights16(imp, (blk % blocks_per_row) * 16, w);
+            uint32_t sb = e4m3_round(a / SM);
+            sb = sb < 1u ? 1u : sb;
+            double best = __builtin_huge_val();
+            int prev = -1;
+            for (int k = lo; k <= hi; ++k) {
+                const int c = clamp_pattern((int)sb + k);
+                if (c == prev)
+                    continue;
+                prev = c;
+                const float4 t = tab[c];
+                const double ef = fpn_error16<N, WMSE>(v, w, t.x, t.y, nullptr);
+                if (ef < best) {
+                    best = ef;
+                    sbyte = (uint32_t)c;
+                }
+                const double ei = intn_error16<N, WMSE>(v, w, t.z, t.w, nullptr);
+                if (ei < best) {
+                    best = ei;
+                    sbyte = (uint32_t)c | 0x80u;
+                }
+            }
+            const float4 t = tab[sbyte & 0x7Fu];
+            if (sbyte & 0x80u)
+                intn_error16<N, WMSE>(v, w, t.z, t.w, cds);
+            else
+                fpn_error16<N, WMSE>(v, w, t.x, t.y, cds);
+        }
+        pack_ifn<N>(cds, words);
+        store_ifn<N>(codes, blk, words);
+        scales[blk] = (uint8_t)sbyte;
+    }
+}
+
+// ---------------------------------------------------------------------------
 // dequantize and error
 // ---------------------------------------------------------------------------
 
 // decode one block's B values (before any un-rotation): FP4 nibbles through
 // the hardware E2M1 decode (exact), times the block step D with one binary32
 // rounding, x_hat = fl32(+-v * D); IF4 INT4 blocks as q * fl32(D * fl32(6/7))
+// 32-bit words of one block's codes
+template <int FMT, int B>
+constexpr int code_words() { return FMT == kIF6 ? 3 : B / 8; }
+
+// value of E2M(n-3) magnitude code m: E2M3 subnormals m/8, then
+// 2^(e-1) (1 + f/8); E2M0 {0, 1, 2, 4}
+template <int N>
+__device__ __forceinline__ float fpn_value(uint32_t m)
+{
+    if constexpr (N == 6)
+        return m < 8u ? (float)m * 0.125f : __uint_as_float(((m >> 3) + 126u) << 23 | (m & 7u) << 20);
+    else
+        return m == 3u ? 4.0f : (float)m;
+}
+
 template <int FMT, int B>
 __device__ __forceinline__ void decode_block(const uint32_t* wds, uint32_t sb, float S, float* o)
 {
+    if constexpr (FMT == kIF3 || FMT == kIF6) {
+        constexpr int N = FMT == kIF6 ? 6 : 3;
+        const uint32_t mag = sb & 0x7Fu;
+        const float D = ((mag == 0x7Fu) ? __builtin_nanf("") : e4m3_value(mag)) * S;
+        const uint64_t lo = (uint64_t)wds[0] | ((uint64_t)wds[1] << 32);
+        const uint64_t hi = N == 6 ? (uint64_t)wds[2] : 0u;
+        const float Di = D * ifn_step<N>();
+#pragma unroll
+        for (int i = 0; i < B; ++i) {
+            const int sh = N * i;
+            uint32_t c = (uint32_t)(sh < 64 ? lo >> sh : hi >> (sh - 64));
+            if (sh < 64 && sh + N > 64)
+                c |= (uint32_t)(hi << (64 - sh));
+            c &= (1u << N) - 1u;
+            if (sb & 0x80u) { // INT: n-bit two's complement
+                const int q = (c >> (N - 1)) ? (int)c - (1 << N) : (int)c;
+                o[i] = (float)q * Di;
+            } else {
+                const float val = fpn_value<N>(c & ((1u << (N - 1)) - 1u)) * D;
+                o[i] = (c >> (N - 1)) ? -val : val;
+            }
+        }
+        return;
+    }
     float D;
     if constexpr (FMT == kMXFP4) {
         D = (sb == 0xFFu) ? __builtin_nanf("")
@@ -1622,10 +1892,19 @@ __device__ __forceinline__ void decode_block(const uint32_t* wds, uint32_t sb, f
     }
 }
 
-template <int B>
+template <int FMT, int B>
 __device__ __forceinline__ void load_codes(const uint8_t* __restrict__ codes, int64_t blk, uint32_t* wds)
 {
-    if constexpr (B == 16) {
+    if constexpr (FMT == kIF6) {        // 12 bytes per block, 4-byte aligned
+        const uint32_t* p = reinterpret_cast<const uint32_t*>(codes) + 3 * blk;
+        wds[0] = p[0];
+        wds[1] = p[1];
+        wds[2] = p[2];
+    } else if constexpr (FMT == kIF3) { // 6 bytes per block, 2-byte aligned
+        const uint16_t* p = reinterpret_cast<const uint16_t*>(codes) + 3 * blk;
+        wds[0] = (uint32_t)p[0] | ((uint32_t)p[1] << 16);
+        wds[1] = (uint32_t)p[2];
+    } else if constexpr (B == 16) {
         const uint2 c = reinterpret_cast<const uint2*>(codes)[blk];
         wds[0] = c.x;
         wds[1] = c.y;
@@ -1654,8 +1933,8 @@ __global__ __launch_bounds__(kThreads) void dequant(
     for (int64_t base = (int64_t)blockIdx.x * kThreads + (threadIdx.x & ~63); base < nblocks; base += stride) {
         const int64_t blk = base + lane;
         if (blk < nblocks) {
-            uint32_t wds[B / 8];
-            load_codes<B>(codes, blk, wds);
+            uint32_t wds[code_words<FMT, B>()];
+            load_codes<FMT, B>(codes, blk, wds);
             float o[B];
             decode_block<FMT, B>(wds, scales[blk], S, o);
             if constexpr (ROT)
@@ -1707,8 +1986,8 @@ __global__ __launch_bounds__(kThreads) void error_partial(
          blk += (int64_t)gridDim.x * kThreads) {
         float v[B], o[B];
         load_block<B, BF16>(x, blk, v);
-        uint32_t wds[B / 8];
-        load_codes<B>(codes, blk, wds);
+        uint32_t wds[code_words<FMT, B>()];
+        load_codes<FMT, B>(codes, blk, wds);
         decode_block<FMT, B>(wds, scales[blk], S, o);
         if constexpr (ROT)
             fwht<B>(o);
@@ -1903,6 +2182,33 @@ static void launch_if4(const QuantArgs& a, int64_t nb, const float* part, int np
     }
 }
 
+template <int N, bool BF16, bool ROT>
+static void launch_ifn(const QuantArgs& a, int64_t nb, const float* part, int npart)
+{
+    const int64_t bpr = a.cols / 16;
+    const int lo = a.rule == kSweep ? a.lo : 0, hi = a.rule == kSweep ? a.hi : 0;
+    // builds an LDS table of the patterns' steps: one round of resident workgroups
+    if (a.objective == kWMSE) {
+        auto k = ifn_quant<N, BF16, ROT, true>;
+        hipLaunchKernelGGL(k, sweep_grid(k, nb), kThreads, 0, a.stream, a.x, nb, bpr, a.importance,
+                           part, npart, a.global_scale, lo, hi, a.codes, a.scales);
+    } else {
+        auto k = ifn_quant<N, BF16, ROT, false>;
+        hipLaunchKernelGGL(k, sweep_grid(k, nb), kThreads, 0, a.stream, a.x, nb, bpr, a.importance,
+                           part, npart, a.global_scale, lo, hi, a.codes, a.scales);
+    }
+}
+
+template <int N>
+static void launch_ifn_dt(const QuantArgs& a, int64_t nb, const float* part, int npart)
+{
+    const bool rot = a.rotate != 0;
+    if (a.bf16)
+        rot ? launch_ifn<N, true, true>(a, nb, part, npart) : launch_ifn<N, true, false>(a, nb, part, npart);
+    else
+        rot ? launch_ifn<N, false, true>(a, nb, part, npart) : launch_ifn<N, false, false>(a, nb, part, npart);
+}
+
 template <bool BF16, bool ROT>
 static void launch_mxfp4(const QuantArgs& a, int64_t nb, int grid)
 {
@@ -1985,6 +2291,10 @@ hipError_t launch_quantize(const QuantArgs& a)
                 rot ? launch_if4<true, true>(a, nb, part, npart, grid) : launch_if4<true, false>(a, nb, part, npart, grid);
             else
                 rot ? launch_if4<false, true>(a, nb, part, npart, grid) : launch_if4<false, false>(a, nb, part, npart, grid);
+        } else if (a.format == kIF6) {
+            launch_ifn_dt<6>(a, nb, part, npart);
+        } else if (a.format == kIF3) {
+            launch_ifn_dt<3>(a, nb, part, npart);
         } else {
             if (a.bf16)
                 rot ? launch_mxfp4<true, true>(a, nb, grid) : launch_mxfp4<true, false>(a, nb, grid);
@@ -2083,6 +2393,10 @@ hipError_t launch_dequantize(const DequantArgs& a)
         launch_dequant_fmt<kNVFP4, 16>(a, nb, grid);
     else if (a.format == kIF4)
         launch_dequant_fmt<kIF4, 16>(a, nb, grid);
+    else if (a.format == kIF6)
+        launch_dequant_fmt<kIF6, 16>(a, nb, grid);
+    else if (a.format == kIF3)
+        launch_dequant_fmt<kIF3, 16>(a, nb, grid);
     else
         launch_dequant_fmt<kMXFP4, 32>(a, nb, grid);
     return hipGetLastError();
@@ -2120,6 +2434,12 @@ hipError_t launch_error(const ErrorArgs& a, double* out_dev)
         else if (a.format == kIF4)
             a.bf16 ? launch_error_fmt<kIF4, 16, true>(a, nb, grid, partials)
                    : launch_error_fmt<kIF4, 16, false>(a, nb, grid, partials);
+        else if (a.format == kIF6)
+            a.bf16 ? launch_error_fmt<kIF6, 16, true>(a, nb, grid, partials)
+                   : launch_error_fmt<kIF6, 16, false>(a, nb, grid, partials);
+        else if (a.format == kIF3)
+            a.bf16 ? launch_error_fmt<kIF3, 16, true>(a, nb, grid, partials)
+                   : launch_error_fmt<kIF3, 16, false>(a, nb, grid, partials);
         else
             a.bf16 ? launch_error_fmt<kMXFP4, 32, true>(a, nb, grid, partials)
                    : launch_error_fmt<kMXFP4, 32, false>(a, nb, grid, partials);

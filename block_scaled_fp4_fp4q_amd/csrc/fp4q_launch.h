@@ -7,7 +7,7 @@
 
 namespace fp4q {
 
-enum { kNVFP4 = 0, kMXFP4 = 1, kIF4 = 2 };
+enum { kNVFP4 = 0, kMXFP4 = 1, kIF4 = 2, kIF3 = 3, kIF6 = 4 };
 enum { kAbsMax = 0, kSweep = 1, kFourSix = 2 };
 enum { kMSE = 0, kWMSE = 1 };
 

@@ -11,6 +11,17 @@
  *   IF4    NVFP4 layout; each block holds either FP4 (E2M1) codes or scaled
  *          INT4 codes, and bit 7 (the sign bit) of its E4M3 scale byte says
  *          which: 0 = FP4, 1 = INT4.
+ *   IF3, IF6  the same adaptive pick at 3 and 6 bits (Adaptive Block-Scaled
+ *          Data Types page, Methodology, which says the idea applies to
+ *          3-bit and 6-bit formats but fixes no grid).  Reading, under which
+ *          n = 4 is exactly IF4: the FP element is E2M(n-3) -- sign, two
+ *          exponent bits with bias 1, n-3 mantissa bits, no inf/NaN (IF3:
+ *          E2M0, magnitudes {0,1,2,4}; IF6: OCP FP6 E2M3, up to 7.5); the
+ *          INT element is an integer in [-(2^(n-1)-1), 2^(n-1)-1] (IF3 +-3,
+ *          IF6 +-31) on the step D*fl32(FPmax/INTmax), which maps the INT
+ *          maximum onto the FP maximum as 6/7 does for IF4; the base scale is
+ *          E4M3(max|x| / (FPmax S)) and a computed global scale is
+ *          S = max|x| / (256 FPmax) (1024 for IF3, 1920 for IF6).
  *
  * Tensor layout.  x is a row-major [rows, cols] tensor; blocks are `block`
  * consecutive elements of one row (cols % block == 0), numbered in memory
@@ -20,6 +31,12 @@
  *           (sign << 3) | magnitude code, magnitudes 0..7 =
  *           {0, 0.5, 1, 1.5, 2, 3, 4, 6}; an INT4 nibble is the 4-bit two's
  *           complement of the integer in [-7, 7].
+ *           IF3 / IF6: [rows*cols*n/8] bytes of n-bit codes, element e at
+ *           bits n*e .. n*e+n-1 of the stream, least significant bit first
+ *           (the nibble layout above is the n = 4 case): 6 bytes per IF3
+ *           block, 12 per IF6 block.  An FP code is (sign << (n-1)) |
+ *           magnitude code (E2M3: (exponent << 3) | mantissa); an INT code
+ *           is the n-bit two's complement.
  *   scales  [rows*cols/block] bytes, one per block in memory order.
  *   S       one fp32 (NVFP4 and IF4 only).
  *
@@ -67,7 +84,7 @@ typedef enum {
     FP4Q_E_SCRATCH = -7      /* more scratch than fp4q_quantize_noalloc has  */
 } fp4q_status;
 
-typedef enum { FP4Q_NVFP4 = 0, FP4Q_MXFP4 = 1, FP4Q_IF4 = 2 } fp4q_format;
+typedef enum { FP4Q_NVFP4 = 0, FP4Q_MXFP4 = 1, FP4Q_IF4 = 2, FP4Q_IF3 = 3, FP4Q_IF6 = 4 } fp4q_format;
 typedef enum { FP4Q_F32 = 0, FP4Q_BF16 = 1 } fp4q_dtype;
 typedef enum {
     FP4Q_SCALE_ABSMAX = 0,
@@ -78,7 +95,7 @@ typedef enum { FP4Q_OBJ_MSE = 0, FP4Q_OBJ_WMSE = 1 } fp4q_objective;
 
 /* The problem statement of one quantization.
  *   format      fp4q_format.
- *   block       16 for NVFP4 and IF4, 32 for MXFP4.
+ *   block       16 for NVFP4, IF4, IF3 and IF6, 32 for MXFP4.
  *   scale_rule  ABSMAX: the block scale is the block maximum mapped onto the
  *               FP4 maximum 6 and rounded to FP8 ("AbsMax", ScaleSweep page,
  *               Problem definition).
@@ -89,9 +106,10 @@ typedef enum { FP4Q_OBJ_MSE = 0, FP4Q_OBJ_WMSE = 1 } fp4q_objective;
  *                 MXFP4: every E8M0 exponent e_base + k ("Bridging the Gap
  *                 ... Microscaling FP4" page, Method 2, format-specific
  *                 scale search).
- *                 IF4: every pattern s_base + k, each with FP4 then with INT4
- *                 codes (the IF4 pick of the Adaptive Block-Scaled Data Types
- *                 page, Methodology, run at every pattern of the window).
+ *                 IF4, IF3, IF6: every pattern s_base + k, each with the FP
+ *                 grid then with the INT grid (the pick of the Adaptive
+ *                 Block-Scaled Data Types page, Methodology, run at every
+ *                 pattern of the window).
  *               FOUR_OVER_SIX (NVFP4 only): the block maximum is mapped onto
  *               6 or onto 4, E4M3(a / (6 S)) vs E4M3(a / (4 S)), and the one
  *               of lower block error kept, 6 on a tie (Adaptive Block-Scaled
@@ -100,7 +118,8 @@ typedef enum { FP4Q_OBJ_MSE = 0, FP4Q_OBJ_WMSE = 1 } fp4q_objective;
  *               encodes; an exact tie keeps the candidate tried first.
  *   objective   MSE, or WMSE weighted by a per-column importance vector
  *               (ScaleSweep page, Method 1).  Used wherever block errors
- *               decide: SWEEP, FOUR_OVER_SIX and IF4's FP4-vs-INT4 pick.
+ *               decide: SWEEP, FOUR_OVER_SIX and the FP-vs-INT pick of IF4,
+ *               IF3 and IF6.
  *   sweep_lo, sweep_hi
  *               the window of offsets, -126 <= lo <= hi <= 126; the pages use
  *               [-3, 7] for MSE and [-8, 7] for WMSE (NVFP4).  An offset that
@@ -135,7 +154,9 @@ size_t fp4q_workspace_bytes(const fp4q_spec* spec, int64_t rows, int64_t cols);
  *               ignored otherwise (may be NULL); 16-byte aligned wherever it
  *               is used (it is read four weights at a time), else
  *               FP4Q_E_ALIGN.
- *   codes       [rows*cols/2] bytes, 8-byte aligned (16 for MXFP4).
+ *   codes       [rows*cols/2] bytes, 8-byte aligned (16 for MXFP4); IF3
+ *               [rows*cols*3/8] bytes, 2-byte aligned; IF6 [rows*cols*3/4]
+ *               bytes, 4-byte aligned.
  *   scales      [rows*cols/block] bytes.
  *   global_scale  one fp32: output (or input when global_scale_given); may be
  *               NULL for MXFP4.
@@ -146,7 +167,9 @@ size_t fp4q_workspace_bytes(const fp4q_spec* spec, int64_t rows, int64_t cols);
  * sign-only codes); each element is encoded as the nearest E2M1 value of
  * |x| * fl32(1 / fl32(s S)) (ties to the even code, saturating at 6).  IF4
  * also encodes the block as integers q = round(|x| / (D 6/7)) clamped to 7
- * and keeps INT4 only when its error is strictly lower.  MXFP4 uses the
+ * and keeps INT4 only when its error is strictly lower; IF3 and IF6 do the
+ * same with their own grids, maxima and steps (see the formats above), the
+ * errors compared in binary64.  MXFP4 uses the
  * power of two 2^(floor(log2 a) - 2).  SWEEP and FOUR_OVER_SIX then choose
  * among the scales listed at fp4q_spec. */
 fp4q_status fp4q_quantize(const fp4q_spec* spec, const void* x, int32_t x_dtype,
@@ -179,8 +202,9 @@ fp4q_status fp4q_quantize_noalloc(const fp4q_spec* spec, const void* x, int32_t 
  * scaling: the quantization scale S_q = S_dq c while the stored
  * dequantization scale stays S_dq; Method 3, dual-granularity scaling: one
  * coefficient c per sub-block of 8 under a shared S_dq).  spec->format is
- * NVFP4 or MXFP4, spec->rotate 0; scale_rule, objective and the window are
- * ignored; global_scale_given as for fp4q_quantize.
+ * NVFP4 or MXFP4 (the adaptive formats give FP4Q_E_UNSUPPORTED),
+ * spec->rotate 0; scale_rule, objective and the window are ignored;
+ * global_scale_given as for fp4q_quantize.
  *   coef        fp32 [rows, cols / coef_group], positive and finite, the
  *               learned relaxation coefficients; row-major, so block b of a
  *               row owns coef[row][b*block/coef_group ...].
@@ -205,9 +229,11 @@ fp4q_status fp4q_quantize_relaxed(const fp4q_spec* spec, const void* x, int32_t 
 /* Dequantize codes/scales/S into y [rows, cols] (y_dtype FP4Q_F32 or
  * FP4Q_BF16, 16-byte aligned): x_hat = +-value(code) * D, D = fl32(s S) for
  * NVFP4/IF4 (fl32(D * fl32(6/7)) for IF4 INT4 blocks, the 6/7 method) or
- * 2^(byte-127) for MXFP4; unrotate (0 or block) applies the block Hadamard,
+ * 2^(byte-127) for MXFP4; IF3 / IF6 INT blocks use D*fl32(4/3) and
+ * D*fl32(7.5/31); unrotate (0 or block) applies the block Hadamard,
  * which is its own inverse.  bf16 output is rounded to nearest even.
- * Alignment: y 16, codes 8 (16 for MXFP4), global_scale 4 bytes. */
+ * Alignment: y 16, codes 8 (16 for MXFP4, 4 for IF6, 2 for IF3), global_scale
+ * 4 bytes. */
 fp4q_status fp4q_dequantize(const fp4q_spec* spec, const uint8_t* codes,
                             const uint8_t* scales, const float* global_scale,
                             int64_t rows, int64_t cols, int32_t unrotate,
@@ -218,8 +244,8 @@ fp4q_status fp4q_dequantize(const fp4q_spec* spec, const uint8_t* codes,
  * / N (NaN when importance is NULL), accumulated in fp64 (ScaleSweep page,
  * Method 1: MSE and WMSE).  x_hat is the dequantized tensor, un-rotated when
  * spec->rotate is set.  Blocks until the two doubles are on the host.
- * Alignment: x 16, codes 8 (16 for MXFP4), workspace 256, global_scale and
- * importance 4 bytes. */
+ * Alignment: x 16, codes 8 (16 for MXFP4, 4 for IF6, 2 for IF3), workspace
+ * 256, global_scale and importance 4 bytes. */
 fp4q_status fp4q_error(const fp4q_spec* spec, const void* x, int32_t x_dtype,
                        int64_t rows, int64_t cols, const float* importance,
                        const uint8_t* codes, const uint8_t* scales,

@@ -532,7 +532,10 @@ double fp4q_ref_fpn_block(int n, const float* xb, int B, const float* w, float S
 }
 
 /* INT branch: step D * fl32(FPmax / INTmax); codes are the n-bit two's
- * complement of the signed integer */
+ * complement of the signed integer.  A zero element is the integer 0
+ * (|x| / D_int = 0), also where D_int < 2^-128 makes ri infinite and
+ * |x| * ri would be NaN: IF6's step 7.5/31 is below 1/4, so the smallest
+ * patterns under the smallest global scales get there. */
 double fp4q_ref_intn_block(int n, const float* xb, int B, const float* w, float S,
                            int c, uint8_t* codes)
 {
@@ -543,8 +546,9 @@ double fp4q_ref_intn_block(int n, const float* xb, int B, const float* w, float 
     double E = 0.0;
     for (int i = 0; i < B; ++i) {
         float a = fabsf(xb[i]);
-        float y = a * ri;
-        int q = fp4q_ref_intn_round(n, y);
+        int q = 0;
+        if (a != 0.0f)
+            q = fp4q_ref_intn_round(n, a * ri);
         float xh = (float)q * Di;
         E = E + elem_err(a, xh, w, i);
         if (codes) {

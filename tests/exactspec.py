@@ -328,13 +328,18 @@ def encode_intn(n, xb, S, c, w=None):
     S = f32(S)
     D = f32(float(E4M3[c])) * S
     Di = D * ifn_step(n)
-    ri = f32(1.0) / Di
+    with np.errstate(divide="ignore", over="ignore"):
+        ri = f32(1.0) / Di
     err, codes = Fr(0), []
     for i, x in enumerate(xb):
         x = f32(x)
         a = abs(x)
-        y = a * ri
-        q = nearest(Fr(float(y)), [Fr(k) for k in range(top + 1)])
+        if a == 0:
+            q = 0   # |x| / D_int = 0, also where 1 / D_int overflows to inf
+        else:
+            with np.errstate(over="ignore"):
+                y = a * ri
+            q = top if np.isinf(y) else nearest(Fr(float(y)), [Fr(k) for k in range(top + 1)])
         xh = f32(q) * Di
         e = (Fr(float(a)) - Fr(float(xh))) ** 2
         if w is not None:

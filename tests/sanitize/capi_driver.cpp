@@ -4,6 +4,7 @@
 // Built with -fsanitize=address,undefined; exits 0 when every check holds.
 #include <cstdint>
 #include <cstdio>
+#include <initializer_list>
 
 #include "fp4q.h"
 
@@ -87,6 +88,21 @@ int main()
     bad = s;
     bad.rotate = 8;
     EXPECT(fp4q_quantize(&bad, x, FP4Q_BF16, 4, 64, nullptr, codes, scales, gs, ws, need, nullptr), FP4Q_E_ARG);
+
+    // IF3 / IF6: their own code alignment (2 and 4 bytes), no Four Over Six
+    for (int fmt : {FP4Q_IF3, FP4Q_IF6}) {
+        fp4q_spec a = spec(fmt);
+        EXPECT(fp4q_quantize(&a, x, FP4Q_BF16, 4, 64, nullptr, codes, scales, gs, ws, need, nullptr), FP4Q_OK);
+        EXPECT(fp4q_quantize(&a, x, FP4Q_BF16, 4, 64, nullptr, codes + (fmt == FP4Q_IF3 ? 1 : 2), scales, gs,
+                             ws, need, nullptr), FP4Q_E_ALIGN);
+        EXPECT(fp4q_dequantize(&a, codes + (fmt == FP4Q_IF3 ? 2 : 4), scales, gs, 4, 64, 0, dev(8), FP4Q_F32,
+                               nullptr), FP4Q_OK);
+        fp4q_spec f = spec(fmt, FP4Q_SCALE_FOUR_OVER_SIX);
+        EXPECT(fp4q_quantize(&f, x, FP4Q_BF16, 4, 64, nullptr, codes, scales, gs, ws, need, nullptr),
+               FP4Q_E_UNSUPPORTED);
+        fp4q_spec wq = spec(fmt, FP4Q_SCALE_ABSMAX, FP4Q_OBJ_WMSE);
+        EXPECT(fp4q_quantize(&wq, x, FP4Q_BF16, 4, 64, nullptr, codes, scales, gs, ws, need, nullptr), FP4Q_E_NULL);
+    }
 
     // the entry point without a workspace
     EXPECT(fp4q_quantize_noalloc(&s, x, FP4Q_BF16, 4, 64, nullptr, codes, scales, gs, nullptr), FP4Q_OK);

@@ -52,7 +52,7 @@ static void run_shape(int64_t rows, int64_t cols, int nthreads)
     float* x = malloc(nn * sizeof(float));
     uint16_t* xb = malloc(nn * sizeof(uint16_t));
     float* imp = malloc((size_t)(cols > 0 ? cols : 1) * sizeof(float));
-    uint8_t* codes = malloc(nn / 2 + 1);
+    uint8_t* codes = malloc(nn * 3 / 4 + 1); /* IF6 needs 6 bits per element */
     uint8_t* scales = malloc(nn / 16 + 1);
     double* best = malloc((nn / 16 + 1) * sizeof(double));
     double* second = malloc((nn / 16 + 1) * sizeof(double));
@@ -66,7 +66,7 @@ static void run_shape(int64_t rows, int64_t cols, int nthreads)
         coef[j] = 0.8f + 0.4f * fabsf(uniform());
 
     const int windows[3][2] = {{-3, 7}, {-8, 7}, {-126, 126}};
-    for (int fmt = 0; fmt < 3; ++fmt) {
+    for (int fmt = 0; fmt <= REF_IF6; ++fmt) {
         const int B = fmt == REF_MXFP4 ? 32 : 16;
         if (cols % B)
             continue;
@@ -105,7 +105,7 @@ static void run_shape(int64_t rows, int64_t cols, int nthreads)
                             }
                         }
         }
-        if (fmt != REF_IF4) {
+        if (fmt == REF_NVFP4 || fmt == REF_MXFP4) {
             for (int group = 8; group <= B; group += B - 8) {
                 for (int sg = 0; sg < 2; ++sg) {
                     float S = 0.0f;
@@ -152,6 +152,15 @@ int main(void)
     CHECK(fp4q_ref_nvfp4_block(v, 16, NULL, 0.01f, 0x30, nib) >= 0.0);
     CHECK(fp4q_ref_int4_block(v, 16, NULL, 0.01f, 0x30, nib) >= 0.0);
     CHECK(fp4q_ref_base_scale(v, 16, 0.01f) >= 0);
+    for (int n = 3; n <= 6; n += 3) {
+        for (int m = 0; m < (1 << (n - 1)); ++m)
+            CHECK(fp4q_ref_fpn_round(n, fp4q_ref_fpn_value(n, m)) == m);
+        CHECK(fp4q_ref_intn_round(n, 1e9f) == (1 << (n - 1)) - 1);
+        CHECK(fp4q_ref_fpn_block(n, v, 16, NULL, 0.01f, 0x30, nib) >= 0.0);
+        CHECK(fp4q_ref_intn_block(n, v, 16, NULL, 0.01f, 0x30, nib) >= 0.0);
+        CHECK(fp4q_ref_ifn_base_scale(n, v, 16, 0.01f) >= 0);
+        CHECK(fp4q_ref_ifn_global_scale(n, 3.0f) > 0.0f);
+    }
 
     /* shapes: empty, one block, ragged row counts, several threads */
     const int64_t shapes[][2] = {{0, 64}, {5, 0}, {1, 32}, {3, 96}, {7, 64}, {33, 160}};

@@ -188,3 +188,21 @@ def test_importance_must_be_16_byte_aligned_where_used(L):
     s = spec(scale_rule=1, objective=1)
     assert q(L, s, imp=C.c_void_p(IMP.value + 4), dtype=B.FP4Q_F32) == -6
     assert q(L, spec(format=2, objective=1), imp=C.c_void_p(IMP.value + 8)) == -6
+
+
+def test_if3_if6_argument_checks(L):
+    # every call below is rejected before any HIP call (the pointers are fake)
+    for fmt, misaligned in ((3, 1), (4, 2)):          # IF3 codes 2-aligned, IF6 4-aligned
+        assert q(L, spec(format=fmt), codes=C.c_void_p(CODES.value + misaligned)) == -6
+        assert q(L, spec(format=fmt, block=32)) == -4                 # block must be 16
+        assert q(L, spec(format=fmt, scale_rule=2)) == -4             # Four Over Six: NVFP4 only
+        assert q(L, spec(format=fmt, objective=1)) == -1              # the pick weighs blocks
+        s = spec(format=fmt)
+        assert L.fp4q_quantize_relaxed(C.byref(s), X, B.FP4Q_BF16, 4, 64, IMP, 8, 0, CODES, SCALES,
+                                       GS, WS, 1 << 20, None) == -4   # no relaxed encode
+    assert q(L, spec(format=5)) == -2
+
+
+def test_code_bytes_per_format():
+    assert B.code_bytes(B.FP4Q_NVFP4, 64) == 32 and B.code_bytes(B.FP4Q_IF4, 64) == 32
+    assert B.code_bytes(B.FP4Q_IF6, 64) == 48 and B.code_bytes(B.FP4Q_IF3, 64) == 24

@@ -235,3 +235,20 @@ def test_hand_worked_blocks(ref, key, n):
 def test_hand_worked_e2m0_ties(ref):
     g = json.load(open(GOLDEN))["fp3_ties_to_even_code"]
     assert [ref.lib().fp4q_ref_fpn_round(3, y) for y in g["y"]] == g["codes"]
+
+
+def test_if6_int_step_below_2_pow_128(ref):
+    # S at its floor 2^-117 and pattern 0x01: D = 2^-126, D_int = D*fl32(7.5/31)
+    # is below 2^-128, so 1/D_int is +inf: zero elements stay INT code 0 and
+    # every nonzero element saturates, on the oracle as in the exact statement
+    S = 2.0 ** -117
+    Di = f32(2.0 ** -126) * f32(ref.lib().fp4q_ref_ifn_step(6))
+    assert Di < f32(2.0 ** -128) and np.isinf(np.float32(1.0) / Di)
+    xb = np.zeros(16, np.float32)
+    xb[1], xb[2], xb[5] = 3e-37, -1e-38, -0.0
+    e, codes = ref.intn_block(6, xb, S, 0x01)
+    assert list(codes[[0, 5]]) == [0, 0] and codes[1] == 31 and codes[2] == (-31) & 63
+    we, wcodes = X.encode_intn(6, xb, S, 0x01)
+    assert list(codes) == wcodes and e == float(we)
+    got = ref.quantize(xb.reshape(1, 16), fmt=ref.IF6, global_scale=S)
+    assert list(ref.unpack_codes(got["codes"], ref.IF6)) == X.quantize_block_ifn(6, xb, S)[1]

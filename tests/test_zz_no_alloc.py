@@ -39,6 +39,8 @@ CASES = [
     ("if4_sweep_rot16", 2, 1, 0, 16, False),
     ("nvfp4_four_over_six", 0, 2, 0, 0, True),
     ("mxfp4_rot32", 1, 0, 0, 32, True),
+    ("if6_sweep", 4, 1, 0, 0, True),
+    ("if3_wmse", 3, 0, 1, 16, False),
 ]
 
 
@@ -56,7 +58,7 @@ def test_noalloc_matches_workspace_call(B, name, fmt, rule, obj, rot, bf16):
         n = rows * cols
         outs = []
         for noalloc in (False, True):
-            codes = torch.full((n // 2,), 0xAB, dtype=torch.uint8, device=DEV)
+            codes = torch.full((B.code_bytes(fmt, n),), 0xAB, dtype=torch.uint8, device=DEV)
             scales = torch.full((n // spec.block,), 0xCD, dtype=torch.uint8, device=DEV)
             gs = torch.full((1,), -1.0, dtype=torch.float32, device=DEV)
             if noalloc:
