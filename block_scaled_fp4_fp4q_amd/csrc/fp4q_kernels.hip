@@ -314,27 +314,8 @@ __device__ __forceinline__ float est_bound(float E, float A, float W, float rel)
     return 16.0f * u * A * __builtin_amdgcn_sqrtf(W * E) * 1.0001f + rel * E + 64.0f * u * u * A * A * W;
 }
 
-// INT4 estimate of IF4's 6/7 method in units of the INT4 step: q =
-// min(RNE(fl(|x| ri)), 7), exactly the method's integer
-template <bool WMSE>
-__device__ __forceinline__ float int4_est16(const float* v, const float* b, float ri)
-{
-    float F = 0.0f;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-        const float z = __builtin_fabsf(v[i]) * ri;
-        const float q = __builtin_fminf(__builtin_rintf(z), 7.0f);
-        float d;
-        if constexpr (WMSE)
-            d = __builtin_fmaf(-b[i], q, b[i] * z);
-        else
-            d = z - q;
-        F = __builtin_fmaf(d, d, F);
-    }
-    return F;
-}
-
-// the same estimate from signed values, also packing the method's INT4
+// INT4 estimate of IF4's 6/7 method in units of the INT4 step, with q the
+// method's integer min(RNE(fl(|x| ri)), 7), also packing the method's INT4
 // nibbles: RNE is odd-symmetric, so q = clamp(rint(v ri), -7, 7) is
 // sign(v) min(RNE(|v| ri), 7), (v ri - q)^2 the same term, and the low four
 // bits of q its two's complement nibble
@@ -1328,27 +1309,93 @@ __global__ __launch_bounds__(kThreads) void nvfp4_foursix(
     }
 }
 
+// INT4 estimate in units of the INT4 step from binary32 fma, add and sub
+// only (the rounding instruction and min issue at half their rate):
+// t = fl(|x| r_int + M), M = 1.5 2^23, holds the exact product rounded to the
+// nearest integer (ties to even) while the product is below 2^22, q = t - M
+// exactly, and d = fl(|x| r_int - q) with a single rounding.  This q differs
+// from the method's RNE(fl(|x| r_int)) only where fl(|x| r_int) is a tie
+// that the exact product is not; |d| then moves by less than one rounding of
+// the product, which the bound's per-element term covers.  CLAMP applies the
+// saturation at 7, needed only where |x| r_int can reach 7.5; without it
+// the product stays below 7.5 by the caller's choice of patterns.
+template <bool WMSE, bool CLAMP>
+__device__ __forceinline__ float int4_est16(const float* v, const float* b, float ri)
+{
+    constexpr float M = 12582912.0f;
+    float F = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        const float a = __builtin_fabsf(v[i]);
+        float t = __builtin_fmaf(a, ri, M);
+        if constexpr (CLAMP)
+            t = __builtin_fminf(t, M + 7.0f);
+        const float q = t - M;
+        float d = __builtin_fmaf(a, ri, -q);
+        if constexpr (WMSE)
+            d = b[i] * d;
+        F = __builtin_fmaf(d, d, F);
+    }
+    return F;
+}
+
+// the two least of non-negative estimates whose low five mantissa bits carry
+// the candidate's place in the window, 2 (k - lo) + (1 for INT4): the place
+// moves an estimate by at most 31 ulp (62u relative), and as unsigned
+// integers +inf and NaN (masked candidates, overflow) order last
+__device__ __forceinline__ void keep_best_packed5(float E, uint32_t k, uint32_t& p1, uint32_t& p2)
+{
+    const uint32_t p = (__float_as_uint(E) & ~0x1Fu) | k;
+    const uint32_t hi = p1 > p ? p1 : p; // p1 <= p2 throughout
+    p2 = p2 < hi ? p2 : hi;
+    p1 = p1 < p ? p1 : p;
+}
+
+// the FP4 and INT4 estimates of one pattern, e = (r, r_int, s^2, (s fl(6/7))^2)
+template <bool WMSE, bool CLAMP>
+__device__ __forceinline__ void if4_pattern(const float* v, const float* b, float4 e, uint32_t place,
+                                            uint32_t& p1, uint32_t& p2)
+{
+    float Ff, unused;
+    fp4_err32<WMSE, false>(v, b, e.x, Ff, unused);
+    keep_best_packed5(Ff * e.z, place, p1, p2);
+    keep_best_packed5(int4_est16<WMSE, CLAMP>(v, b, e.y) * e.w, place + 1u, p1, p2);
+}
+
 // IF4 over a window of patterns: per pattern the FP4 then the INT4 encoding,
 // the first least binary64 error kept.  Certified binary32 estimates decide
-// when the two least are separated; the rest run the exact search.
+// when the two least are separated; the other blocks join a per-wave LDS
+// queue that the wave drains with the exact search, sixteen lanes per block.
+// A wave's queue and its drain involve that wave alone, so the grid-stride
+// loop has no workgroup barrier and the waves of a workgroup never wait for
+// each other.  Six waves per SIMD for MSE (80 VGPRs, no spills) ran faster
+// than the five the compiler picks by itself.
 template <bool BF16, bool ROT, bool WMSE>
-__global__ __launch_bounds__(kThreads) void if4_sweep(
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(WMSE ? 4 : 6))) void if4_sweep(
     const void* __restrict__ x, int64_t nblocks, int64_t blocks_per_row,
     const float* __restrict__ imp, const float* __restrict__ partials, int npart,
     float* __restrict__ Sp, int lo, int hi, uint2* __restrict__ codes, uint8_t* __restrict__ scales)
 {
-    __shared__ float4 tab[128];  // D, r, D_int = fl32(D 6/7), r_int
-    __shared__ float2 tab2[128]; // s^2 and (s 6/7)^2: the estimates' units over S^2
+    __shared__ float4 tab[128]; // D, r, D_int = fl32(D 6/7), r_int
+    // per index c = clamp(s_base + k, 0, 127): r, r_int and the estimates'
+    // units s^2 and (s fl(6/7))^2 over S^2.  Indices 0 and 127 stand for
+    // offsets past patterns 0x01 and 0x7E, which repeat an end pattern: their
+    // units are +inf, so those candidates order last.
+    __shared__ float4 est[128];
+    __shared__ int64_t queue[kThreads / 64][128]; // per wave: uncertified blocks
+    __shared__ float stage[kThreads / 16][WMSE ? 2 : 1][16]; // a queued block and its weights per group
     __shared__ __attribute__((aligned(16))) float root[WMSE ? kRootCols : 1]; // read as float4
     __shared__ float wsum[WMSE ? kRootCols / 16 : 1];
     const float S = global_scale(partials, npart, Sp);
     for (int c = threadIdx.x; c < 128; c += kThreads) {
-        const float sv = e4m3_value((uint32_t)(c < 0x7E ? c : 0x7E));
+        const int ce = c < 1 ? 1 : (c > 0x7E ? 0x7E : c);
+        const float sv = e4m3_value((uint32_t)ce);
         const float D = sv * S;
         const float Di = D * kInt4Step;
         tab[c] = make_float4(D, 1.0f / D, Di, 1.0f / Di);
         const float sz = sv * kInt4Step;
-        tab2[c] = make_float2(sv * sv, sz * sz);
+        const float inf = __builtin_huge_valf();
+        est[c] = make_float4(1.0f / D, 1.0f / Di, c == ce ? sv * sv : inf, c == ce ? sz * sz : inf);
     }
     bool roots_in_lds = false;
     if constexpr (WMSE)
@@ -1356,80 +1403,210 @@ __global__ __launch_bounds__(kThreads) void if4_sweep(
     __syncthreads();
     const float S6 = 6.0f * S, invS = 1.0f / S;
     constexpr float u = 0x1p-24f;
-    for (int64_t blk = (int64_t)blockIdx.x * kThreads + threadIdx.x; blk < nblocks;
-         blk += (int64_t)gridDim.x * kThreads) {
-        float v[16];
-        load_block<16, BF16>(x, blk, v);
-        if constexpr (ROT)
-            fwht<16>(v);
-        const float a = block_absmax<16>(v);
-        uint2 packed;
-        uint32_t sbyte = 0;
-        if (a == 0.0f) {
-            packed = fp4_encode16(v, 1.0f);
-        } else {
-            uint32_t sb = e4m3_round(a / S6);
-            sb = sb < 1u ? 1u : sb;
-            const int64_t col0 = (blk % blocks_per_row) * 16;
-            const int ctop = clamp_pattern((int)sb + hi);
-            // estimates of every (pattern, type) in the method's order
-            float b[16];
-            float W = 16.0f;
-            if constexpr (WMSE)
-                block_roots<16>(imp, root, wsum, roots_in_lds, col0, b, W);
-            float e1 = __builtin_huge_valf(), e2 = __builtin_huge_valf();
-            int cb = (int)sb, cprev = -1;
-            for (int k = lo; k <= hi; ++k) {
-                const int c = clamp_pattern((int)sb + k);
-                if (c == cprev)
-                    continue;
-                cprev = c;
-                const float4 t = tab[c];
-                const float2 t2 = tab2[c];
-                float Ff, unused;
-                fp4_err32<WMSE, false>(v, b, t.y, Ff, unused);
-                keep_best(Ff * t2.x, c, e1, e2, cb);
-                keep_best(int4_est16<WMSE>(v, b, t.w) * t2.y, c | 0x80, e1, e2, cb);
-            }
-            const float A = __builtin_fmaxf(a * invS * (1.0f + 4.0f * u),
-                                            6.0f * e4m3_value((uint32_t)ctop)) * (1.0f + 4.0f * u);
-            const float t1 = est_bound(e1, A, W, 40.0f * u), t2 = est_bound(e2, A, W, 40.0f * u);
-            const float4 tt = tab[ctop];
-            const bool finite = 6.0f * tt.x < __builtin_huge_valf() && 7.0f * tt.z < __builtin_huge_valf();
-            const bool certain = finite && e1 < __builtin_huge_valf() &&
-                                 (e2 == __builtin_huge_valf() || e2 - t2 > e1 + t1);
-            if (!certain) { // exact binary64 search
-                float w[16];
-                if constexpr (WMSE)
-                    load_weights16(imp, col0, w);
-                double best = 0.0;
-                cb = (int)sb;
-                cprev = -1;
-                for (int k = lo; k <= hi; ++k) {
-                    const int c = clamp_pattern((int)sb + k);
-                    if (c == cprev)
-                        continue;
-                    const float4 t = tab[c];
-                    const double Ef = fp4_error16<WMSE>(v, w, t.x, t.y);
-                    if (cprev < 0 || Ef < best) { // the first candidate is always taken
-                        best = Ef;
-                        cb = c;
+    const bool packed = hi - lo <= 15; // 2 (hi - lo + 1) places fit five bits
+
+    // exact binary64 search of the queued blocks: lane `sub` of a group of 16
+    // takes the offsets lo + sub, lo + sub + 16, ...; the group keeps the
+    // least (error, 2 c + type) pair, which is the first least error in the
+    // method's order (patterns ascending, FP4 before INT4).  The block (and
+    // its weights) pass through LDS and the error sums run element by
+    // element in a loop that is not unrolled: the same terms in the same
+    // order as fp4_error16 / int4_error16 with few live registers, so that
+    // this rare path does not set the kernel's register budget.
+    const int wv = threadIdx.x >> 6;
+    auto wave_sync = [] {
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    };
+    auto drain = [&](uint32_t n) {
+        const int grp = threadIdx.x >> 4, sub = threadIdx.x & 15;
+        for (uint32_t j0 = 0; j0 < n; j0 += 4) {
+            const uint32_t j = j0 + (uint32_t)(grp & 3);
+            const bool active = j < n;
+            const int64_t blk = queue[wv][active ? j : 0];
+            uint32_t sb;
+            {
+                float v[16];
+                load_block<16, BF16, false>(x, blk, v);
+                if constexpr (ROT)
+                    fwht<16>(v);
+                const float a = block_absmax<16>(v);
+                sb = e4m3_round(a / S6);
+                sb = sb < 1u ? 1u : sb;
+                if (sub == 0) {
+#pragma unroll
+                    for (int i = 0; i < 16; ++i)
+                        stage[grp][0][i] = v[i];
+                    if constexpr (WMSE) {
+                        const int64_t col0 = (blk % blocks_per_row) * 16;
+#pragma unroll
+                        for (int i = 0; i < 16; ++i)
+                            stage[grp][WMSE ? 1 : 0][i] = imp[col0 + i];
                     }
-                    const double Ei = int4_error16<WMSE>(v, w, t.z, t.w);
-                    if (Ei < best) {
-                        best = Ei;
-                        cb = c | 0x80;
-                    }
-                    cprev = c;
                 }
             }
-            const float4 t = tab[cb & 0x7F];
-            packed = (cb & 0x80) ? encode16_int4(v, t.w) : fp4_encode16(v, t.y);
-            sbyte = (uint32_t)cb;
+            wave_sync();
+            const float* xs = stage[grp][0];
+            const float* ws = stage[grp][WMSE ? 1 : 0]; // read only with weights
+            double best = __builtin_huge_val();
+            int key = 0x7FFF;
+            for (int k = lo + sub; k <= hi; k += 16) {
+                const int c = clamp_pattern((int)sb + k);
+                const float4 t = tab[c];
+                double ef = 0.0, ei = 0.0;
+#pragma unroll 1
+                for (int i = 0; i < 16; ++i) {
+                    const float a = __builtin_fabsf(xs[i]);
+                    const float xf = e2m1_q(a * t.y) * t.x;
+                    const float xi = __builtin_fminf(__builtin_rintf(a * t.w), 7.0f) * t.z;
+                    const double df = (double)a - (double)xf;
+                    const double di = (double)a - (double)xi;
+                    double tf = df * df, ti = di * di;
+                    if constexpr (WMSE) {
+                        const double wi = (double)ws[i];
+                        tf = wi * tf;
+                        ti = wi * ti;
+                    }
+                    ef = ef + tf;
+                    ei = ei + ti;
+                }
+                if (ef < best || (ef == best && 2 * c < key)) {
+                    best = ef;
+                    key = 2 * c;
+                }
+                if (ei < best || (ei == best && 2 * c + 1 < key)) {
+                    best = ei;
+                    key = 2 * c + 1;
+                }
+            }
+#pragma unroll
+            for (int off = 8; off > 0; off >>= 1) {
+                const double E2 = __shfl_xor(best, off, 64);
+                const int k2 = __shfl_xor(key, off, 64);
+                if (E2 < best || (E2 == best && k2 < key)) {
+                    best = E2;
+                    key = k2;
+                }
+            }
+            if (active && sub == 0) {
+                float v[16];
+#pragma unroll
+                for (int i = 0; i < 16; ++i)
+                    v[i] = xs[i];
+                const float4 t = tab[key >> 1];
+                codes[blk] = (key & 1) ? encode16_int4(v, t.w) : fp4_encode16(v, t.y);
+                scales[blk] = (uint8_t)((key >> 1) | ((key & 1) << 7));
+            }
+            wave_sync(); // the stage is rewritten next round
         }
-        codes[blk] = packed;
-        scales[blk] = (uint8_t)sbyte;
+    };
+
+    // every lane of a wave runs the same number of iterations, so the
+    // wave-wide queue count and drain stay uniform
+    uint32_t wq = 0; // entries in this wave's queue (the same in every lane)
+    const int64_t stride = (int64_t)gridDim.x * kThreads;
+    for (int64_t base = (int64_t)blockIdx.x * kThreads; base < nblocks; base += stride) {
+        const int64_t blk = base + threadIdx.x;
+        bool queued = false;
+        if (blk < nblocks) {
+            float v[16];
+            load_block<16, BF16>(x, blk, v);
+            if constexpr (ROT)
+                fwht<16>(v);
+            const float a = block_absmax<16>(v);
+            if (a == 0.0f) {
+                codes[blk] = fp4_encode16(v, 1.0f); // signs only
+                scales[blk] = 0;
+            } else {
+                uint32_t sb = e4m3_round(a / S6);
+                sb = sb < 1u ? 1u : sb;
+                const int64_t col0 = (blk % blocks_per_row) * 16;
+                const int ctop = clamp_pattern((int)sb + hi);
+                float b[16];
+                float W = 16.0f;
+                if constexpr (WMSE)
+                    block_roots<16>(imp, root, wsum, roots_in_lds, col0, b, W);
+                float e1, e2, rel;
+                int cb;
+                if (packed) {
+                    uint32_t p1 = 0x7F800000u, p2 = 0x7F800000u;
+                    // below s_base |x| r_int can reach 7.5: saturate
+                    for (int k = lo; k <= (hi < -1 ? hi : -1); ++k)
+                        if4_pattern<WMSE, true>(v, b, est[(int)sb + k < 0 ? 0 : (int)sb + k],
+                                                2u * (uint32_t)(k - lo), p1, p2);
+                    if (lo <= 0 && hi >= 0) {
+                        // at s_base, |x| r_int < 7 (17/16) < 7.5 unless
+                        // s_base is subnormal or saturated
+                        const float4 e = est[sb];
+                        if (__builtin_amdgcn_ballot_w64(sb < 8u || sb >= 0x7Eu) != 0)
+                            if4_pattern<WMSE, true>(v, b, e, 2u * (uint32_t)(-lo), p1, p2);
+                        else
+                            if4_pattern<WMSE, false>(v, b, e, 2u * (uint32_t)(-lo), p1, p2);
+                    }
+                    // above s_base, |x| r_int < 7 (31/32) < 7
+                    for (int k = lo > 1 ? lo : 1; k <= hi; ++k)
+                        if4_pattern<WMSE, false>(v, b, est[(int)sb + k > 127 ? 127 : (int)sb + k],
+                                                 2u * (uint32_t)(k - lo), p1, p2);
+                    e1 = p1 < 0x7F800000u ? __uint_as_float(p1) : __builtin_huge_valf();
+                    e2 = p2 < 0x7F800000u ? __uint_as_float(p2) : __builtin_huge_valf();
+                    const uint32_t place = p1 & 0x1Fu;
+                    cb = ((int)sb + lo + (int)(place >> 1)) | ((place & 1u) ? 0x80 : 0);
+                    rel = 104.0f * u; // 40u, + 62u from the packed places
+                } else {
+                    // wide windows: every distinct pattern once, in order
+                    e1 = __builtin_huge_valf();
+                    e2 = __builtin_huge_valf();
+                    cb = (int)sb;
+                    int cprev = -1;
+                    for (int k = lo; k <= hi; ++k) {
+                        const int c = clamp_pattern((int)sb + k);
+                        if (c == cprev)
+                            continue;
+                        cprev = c;
+                        const float4 e = est[c];
+                        float Ff, unused;
+                        fp4_err32<WMSE, false>(v, b, e.x, Ff, unused);
+                        keep_best(Ff * e.z, c, e1, e2, cb);
+                        keep_best(int4_est16<WMSE, true>(v, b, e.y) * e.w, c | 0x80, e1, e2, cb);
+                    }
+                    rel = 40.0f * u;
+                }
+                const float A = __builtin_fmaxf(a * invS * (1.0f + 4.0f * u),
+                                                6.0f * e4m3_value((uint32_t)ctop)) * (1.0f + 4.0f * u);
+                const float t1 = est_bound(e1, A, W, rel), t2 = est_bound(e2, A, W, rel);
+                const float4 tt = tab[ctop];
+                // the top pattern's reconstructions finite (the exact search
+                // sees overflow)
+                const bool finite = 6.0f * tt.x < __builtin_huge_valf() && 7.0f * tt.z < __builtin_huge_valf();
+                const bool certain = finite && e1 < __builtin_huge_valf() &&
+                                     (e2 == __builtin_huge_valf() || e2 - t2 > e1 + t1);
+                if (certain) {
+                    const float4 t = tab[cb & 0x7F];
+                    codes[blk] = (cb & 0x80) ? encode16_int4(v, t.w) : fp4_encode16(v, t.y);
+                    scales[blk] = (uint8_t)cb;
+                } else {
+                    queued = true;
+                }
+            }
+        }
+        {
+            const uint64_t m = __builtin_amdgcn_ballot_w64(queued);
+            if (queued) {
+                const uint32_t below = __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
+                                                                 __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+                queue[wv][wq + below] = blk;
+            }
+            wq += (uint32_t)__builtin_popcountll(m);
+            if (wq > 64u) { // at most 64 join per iteration: drain before overflow
+                wave_sync();
+                drain(wq);
+                wq = 0;
+            }
+        }
     }
+    wave_sync();
+    drain(wq);
 }
 
 // the eight codes of v[0..7] * r, r = fl32(1 / D_q).  When D_q is below

@@ -180,7 +180,8 @@ def test_bound_is_not_vacuous(ref):
 
 
 def int4_estimate(v, w, S, c, mse):
-    """IF4's INT4 estimate at pattern c in units of S^2: q = min(RNE(fl(|x| ri)), 7)."""
+    """IF4's INT4 estimate at pattern c in units of S^2 (the single-pattern
+    IF4 kernel): q = min(RNE(fl(|x| ri)), 7), the method's integer."""
     s = E4M3[c]
     D = (s * f32(S)).astype(f32)
     Di = (D * f32(6.0 / 7.0)).astype(f32)
@@ -197,6 +198,106 @@ def int4_estimate(v, w, S, c, mse):
         F = fma32(d, d, F)
     sz = (s * f32(6.0 / 7.0)).astype(f32)
     return (F * (sz * sz).astype(f32)).astype(f32)
+
+
+def int4_estimate_magic(v, w, S, c, mse, clamp=True):
+    """The IF4 window kernel's INT4 estimate at pattern c in units of S^2:
+    t = fl(|x| ri + 1.5 2^23) rounds the exact product p = |x| ri to the
+    nearest integer (ties to even), q = t - 1.5 2^23 (saturated at 7 when
+    clamp), d = fl(p - q) with one rounding.  p is exact in binary64 (two
+    24-bit factors), so RNE(p) and p - q are exact there too."""
+    s = E4M3[c]
+    D = (s * f32(S)).astype(f32)
+    Di = (D * f32(6.0 / 7.0)).astype(f32)
+    ri = (f32(1) / Di).astype(f32)
+    p = np.abs(v).astype(f64) * ri.astype(f64)[:, None]
+    q = np.rint(p)
+    if clamp:
+        q = np.minimum(q, 7.0)
+    d = (p - q).astype(f32)
+    b = np.sqrt(w).astype(f32)
+    F = np.zeros(v.shape[0], f32)
+    for i in range(16):
+        e = d[:, i] if mse else (b[:, i] * d[:, i]).astype(f32)
+        F = fma32(e, e, F)
+    sz = (s * f32(6.0 / 7.0)).astype(f32)
+    return (F * (sz * sz).astype(f32)).astype(f32)
+
+
+def int4_window_blocks(ref, seed):
+    """Uniform and heavy-tailed blocks, plus blocks whose maximum sits just
+    below an E4M3 rounding boundary of max/(6S) (the largest |x| r_int for
+    the pattern s_base and the ones above it), with their S and s_base."""
+    rng = np.random.default_rng(seed)
+    v = np.concatenate([rng.uniform(-1, 1, (300, 16)), student(300, seed + 1, scale=0.1)]).astype(np.float32)
+    L = ref.lib()
+    S = L.fp4q_ref_global_scale(f32(np.abs(v).max()))
+    # push each of 200 blocks' maximum to just below the midpoint above its
+    # E4M3 pattern (normal and subnormal patterns alike)
+    extra = rng.uniform(-1, 1, (200, 16)).astype(np.float32) * f32(0.01)
+    for i in range(200):
+        pat = int(rng.integers(1, 0x7D))
+        mid = (float(E4M3[pat]) + float(E4M3[pat + 1])) / 2 * 6 * float(S)
+        m = np.nextafter(f32(mid), f32(0))
+        for _ in range(int(rng.integers(0, 4))):
+            m = np.nextafter(m, f32(0))
+        extra[i] *= float(m)
+        extra[i, int(rng.integers(0, 16))] = m * (1 if rng.random() < 0.5 else -1)
+    v = np.concatenate([v, extra]).astype(np.float32)
+    a = np.abs(v).max(1)
+    sb = np.array([max(1, L.fp4q_ref_e4m3_round(f32(x))) for x in (a / (f32(6) * f32(S))).astype(f32)])
+    return v, S, a, sb
+
+
+def test_int4_saturation_only_below_s_base(ref):
+    # the window kernel skips the saturation at 7 for patterns above s_base,
+    # and at s_base itself when s_base is normal and not the top pattern: there
+    # every |x| r_int stays below 7.5, so min(RNE(|x| r_int), 7) = RNE(|x| r_int)
+    v, S, a, sb = int4_window_blocks(ref, 21)
+    for k in range(0, 8):
+        c = sb + k
+        ok = (c <= 0x7E) & ((k > 0) | ((sb >= 8) & (sb < 0x7E)))
+        D = (E4M3[np.minimum(c, 0x7E)] * f32(S)).astype(f32)
+        ri = (f32(1) / (D * f32(6.0 / 7.0)).astype(f32)).astype(f32)
+        p = a.astype(f64) * ri.astype(f64)
+        assert p[ok].max() < 7.5
+        if k > 0:
+            assert p[ok].max() < 7.0
+    # and below s_base saturation does occur (the clamp is needed there)
+    c = np.maximum(sb - 1, 1)
+    ri = (f32(1) / ((E4M3[c] * f32(S)).astype(f32) * f32(6.0 / 7.0)).astype(f32)).astype(f32)
+    assert (a.astype(f64) * ri.astype(f64)).max() >= 7.5
+
+
+@pytest.mark.parametrize("mse", [True, False])
+def test_bound_int4_window_estimate(ref, mse):
+    # the window kernel's INT4 estimates (rounding through 1.5 2^23), clamped
+    # below s_base and not above, against the oracle's binary64 INT4 errors
+    v, S, a, sb = int4_window_blocks(ref, 23)
+    rng = np.random.default_rng(24)
+    w = rng.lognormal(0, 2, v.shape).astype(np.float32)
+    W = np.full(len(v), 16.0)
+    if not mse:
+        Wf = np.zeros(len(v), f32)
+        for i in range(16):
+            Wf = (Wf + w[:, i]).astype(f32)
+        W = Wf.astype(f64)
+    worst = 0.0
+    for k in range(-3, 8):
+        c = np.clip(sb + k, 1, 0x7E)
+        real = (sb + k >= 1) & (sb + k <= 0x7E)
+        ctop = np.clip(sb + 7, 1, 0x7E)
+        A = np.maximum(a.astype(f64) * f64(f32(1) / f32(S)) * (1 + 4 * U),
+                       6 * E4M3[ctop].astype(f64)) * (1 + 4 * U)
+        E = int4_estimate_magic(v, w, S, c, mse).astype(f64)
+        if k > 0:
+            # the kernel's unclamped form (above s_base) agrees wherever it is used
+            Eu = int4_estimate_magic(v, w, S, c, mse, clamp=False).astype(f64)
+            assert np.array_equal(E[real], Eu[real])
+        ex = np.array([ref.int4_block(v[i], S, int(c[i]), None if mse else w[i])[0] for i in range(len(v))])
+        ex = ex / (f64(S) * f64(S))
+        worst = max(worst, float((np.abs(ex - E) / bound(E, A, W, 40 * U)).max()))
+    assert worst <= 1.0
 
 
 @pytest.mark.parametrize("mse", [True, False])

@@ -143,11 +143,40 @@ def test_if4_window(B, ref, dtype, rotate, objective):
     assert 0.0 < ind.mean() < 1.0
 
 
-@pytest.mark.parametrize("window", [(0, 0), (-126, 126), (-8, 7), (4, 9)])
+@pytest.mark.parametrize("window", [(0, 0), (-126, 126), (-8, 7), (4, 9), (-5, -2), (-9, 6)])
 def test_if4_windows_and_given_scale(B, ref, window):
     x = synth.c4(rows=9, cols=256, seed=62)[0]
     compare(B, ref, x, B.FP4Q_IF4, B.FP4Q_SCALE_SWEEP, 0, window=window)
     compare(B, ref, x, B.FP4Q_IF4, B.FP4Q_SCALE_SWEEP, 0, window=window, given=0.004)
+    # a given S this small saturates s_base at 0x7E for most blocks
+    compare(B, ref, x, B.FP4Q_IF4, B.FP4Q_SCALE_SWEEP, 0, window=window, given=1e-4)
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("objective", [0, 1])
+def test_if4_window_exact_ties_everywhere(B, ref, objective):
+    # three blocks in four are one element 6 S (E4M3 1.0) among zeros under a
+    # given S = 1/16: FP4 codes at patterns 1.0 (code 6) and 1.5 (code 4)
+    # both reconstruct it exactly, an exact tie that no estimate certifies.
+    # With 786432 blocks every wave meets more than 64 of them and drains its
+    # queue inside the grid-stride loop as well as at the end.  The remaining
+    # blocks mix random values with tiny ones (subnormal s_base).
+    rows, cols = 6144, 2048
+    rng = np.random.default_rng(66 + objective)
+    x = np.zeros((rows * cols // 16, 16), np.float32)
+    kind = rng.integers(0, 4, x.shape[0])
+    tie = kind < 3
+    x[np.nonzero(tie)[0], rng.integers(0, 16, tie.sum())] = 0.375
+    n = (~tie).sum()
+    vals = rng.standard_normal((n, 16)).astype(np.float32) * np.float32(0.2)
+    vals[::7] *= np.float32(2.0 ** -14)          # s_base in E4M3's subnormal range
+    x[~tie] = vals
+    x = x.reshape(rows, cols)
+    imp = weights(cols, 67)
+    s, _ = compare(B, ref, x, B.FP4Q_IF4, B.FP4Q_SCALE_SWEEP, objective, window=(-3, 7), imp=imp,
+                   given=1.0 / 16)
+    # the first zero error in the method's order: FP4 at s_base = E4M3 1.0
+    assert np.all(s[tie] == 0x38)
 
 
 def test_extension_edge_blocks(B, ref):
