@@ -420,7 +420,7 @@ __global__ __launch_bounds__(kThreads) void nvfp4_absmax(
 // when the runner-up minus its bound exceeds the best plus its bound, the
 // binary64 argmin (ties to the smaller byte) is the estimated one.  Blocks
 // that are not certified -- exact ties, near ties, all-on-grid blocks -- go to
-// a queue in LDS that the whole workgroup drains with the exact binary64
+// a per-wave queue in LDS that the wave drains with the exact binary64
 // evaluation, so the result equals the binary64 sweep for every block.
 // ---------------------------------------------------------------------------
 
@@ -543,8 +543,6 @@ __device__ __forceinline__ void sweep_fixed(const float* v, const float* b, cons
     }
 }
 
-constexpr int kQueueHalf = 512; // fallback queue entries per workgroup and parity (LDS)
-
 template <bool BF16, bool ROT, bool WMSE, int WIN>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) void nvfp4_sweep(
     const void* __restrict__ x, int64_t nblocks, int64_t blocks_per_row,
@@ -556,10 +554,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
     // serves both), else 0.  Estimates are kept in units of S^2: s*s is
     // normal for every pattern, while D*D would underflow for small S.
     __shared__ float4 tab[128];
-    // uncertified blocks: iterations of even and odd index append to their
-    // own half, so a half's count is stable while it is checked
-    __shared__ int64_t queue[2][kQueueHalf];
-    __shared__ uint32_t qn[2];
+    // uncertified blocks, one queue per wave: a wave appends at most 64 per
+    // iteration and drains its queue once it holds more than 64
+    __shared__ int64_t queue[kThreads / 64][128];
+    __shared__ float stage[kThreads / 16][WMSE ? 2 : 1][16]; // a queued block and its weights per group
     // sqrt(importance) per column and the importance sum per block column
     __shared__ __attribute__((aligned(16))) float root[WMSE ? kRootCols : 1]; // read as float4
     __shared__ float wsum[WMSE ? kRootCols / 16 : 1];
@@ -574,8 +572,6 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
     bool roots_in_lds = false;
     if constexpr (WMSE)
         roots_in_lds = roots_prologue(imp, blocks_per_row * 16, root, wsum);
-    if (threadIdx.x < 2)
-        qn[threadIdx.x] = 0;
     __syncthreads();
     // every pair (c, c+8) with c in [8, 0x76] an exact doubling (true unless S
     // pushes the steps to the ends of the binary32 range)
@@ -592,33 +588,68 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
         col_step = stride % blocks_per_row;
     }
 
-    // Exact binary64 sweep of the queued blocks, candidate-parallel: sixteen
-    // lanes share a block, each evaluates every sixteenth offset of the
-    // window, and the group keeps the least (error, pattern) pair -- the same
-    // choice as a scan in ascending order that keeps the first least error.
-    auto drain = [&](int h) {
-        const uint32_t n = qn[h];
+    // Exact binary64 sweep of a wave's queued blocks, candidate-parallel:
+    // sixteen lanes share a block, each evaluates every sixteenth offset of
+    // the window, and the group keeps the least (error, pattern) pair -- the
+    // same choice as a scan in ascending order that keeps the first least
+    // error.  The block (and its weights) pass through LDS and each error sum
+    // runs element by element in a loop that is not unrolled, with the terms
+    // and order of fp4_error16: few live registers, so this rare path does
+    // not set the register budget of the common one.  A wave's queue and
+    // drain involve that wave alone: the grid-stride loop has no workgroup
+    // barrier.
+    const int wv = threadIdx.x >> 6;
+    auto wave_sync = [] {
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    };
+    auto drain = [&](uint32_t n) {
         const int grp = threadIdx.x >> 4, sub = threadIdx.x & 15;
-        for (uint32_t j0 = 0; j0 < n; j0 += kThreads / 16) {
-            const uint32_t j = j0 + grp;
+        for (uint32_t j0 = 0; j0 < n; j0 += 4) {
+            const uint32_t j = j0 + (uint32_t)(grp & 3);
             const bool active = j < n;
-            const int64_t blk = queue[h][active ? j : 0];
-            float v[16];
-            load_block<16, BF16, false>(x, blk, v);
-            if constexpr (ROT)
-                fwht<16>(v);
-            const float a = block_absmax<16>(v);
-            uint32_t sb = e4m3_round(a / S6);
-            sb = sb < 1u ? 1u : sb;
-            float w[16];
-            if constexpr (WMSE)
-                load_weights16(imp, (blk % blocks_per_row) * 16, w);
+            const int64_t blk = queue[wv][active ? j : 0];
+            uint32_t sb;
+            {
+                float v[16];
+                load_block<16, BF16, false>(x, blk, v);
+                if constexpr (ROT)
+                    fwht<16>(v);
+                const float a = block_absmax<16>(v);
+                sb = e4m3_round(a / S6);
+                sb = sb < 1u ? 1u : sb;
+                if (sub == 0) {
+#pragma unroll
+                    for (int i = 0; i < 16; ++i)
+                        stage[grp][0][i] = v[i];
+                    if constexpr (WMSE) {
+                        const int64_t col0 = (blk % blocks_per_row) * 16;
+#pragma unroll
+                        for (int i = 0; i < 16; ++i)
+                            stage[grp][WMSE ? 1 : 0][i] = imp[col0 + i];
+                    }
+                }
+            }
+            wave_sync();
+            const float* xs = stage[grp][0];
+            const float* ws = stage[grp][WMSE ? 1 : 0]; // read only with weights
             double best = __builtin_huge_val();
             int cb = 0x7F;
             for (int k = lo + sub; k <= hi; k += 16) {
                 const int c = clamp_pattern((int)sb + k);
                 const float4 t = tab[c];
-                const double E = fp4_error16<WMSE>(v, w, t.x, t.y);
+                double E = 0.0;
+#pragma unroll 1
+                for (int i = 0; i < 16; ++i) {
+                    const float a = __builtin_fabsf(xs[i]);
+                    const float xh = e2m1_q(a * t.y) * t.x;
+                    const double d = (double)a - (double)xh;
+                    double tt = d * d;
+                    if constexpr (WMSE)
+                        tt = (double)ws[i] * tt;
+                    E = E + tt;
+                }
                 if (E < best || (E == best && c < cb)) {
                     best = E;
                     cb = c;
@@ -634,19 +665,20 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
                 }
             }
             if (active && sub == 0) {
+                float v[16];
+#pragma unroll
+                for (int i = 0; i < 16; ++i)
+                    v[i] = xs[i];
                 codes[blk] = fp4_encode16(v, tab[cb].y);
                 scales[blk] = (uint8_t)cb;
             }
+            wave_sync(); // the stage is rewritten next round
         }
-        __syncthreads();
-        if (threadIdx.x == 0)
-            qn[h] = 0;
-        __syncthreads();
     };
+    uint32_t wq = 0; // entries in this wave's queue (the same in every lane)
 
-    // every thread runs the same number of iterations, so the barriers below
-    // are reached uniformly
-    int h = 0; // queue half of this iteration
+    // every lane of a wave runs the same number of iterations, so the queue
+    // count and the drain stay wave-uniform
     // bf16 input of this lane's next block, loaded one iteration ahead so that
     // its latency overlaps the current block's arithmetic (8 VGPRs; binary32
     // input loads in place)
@@ -659,8 +691,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
             pre[1] = __builtin_nontemporal_load(p + 1);
         }
     }
-    for (int64_t base = (int64_t)blockIdx.x * kThreads; base < nblocks; base += stride, h ^= 1) {
+    for (int64_t base = (int64_t)blockIdx.x * kThreads; base < nblocks; base += stride) {
         const int64_t blk = base + threadIdx.x;
+        bool queued = false;
         if (blk < nblocks) {
             float v[16];
             if constexpr (BF16) {
@@ -683,7 +716,6 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
             if constexpr (ROT)
                 fwht<16>(v);
             const float a = block_absmax<16>(v);
-            bool queued = false;
             if (a == 0.0f) {
                 codes[blk] = fp4_encode16(v, 1.0f); // signs only
                 scales[blk] = 0;
@@ -767,25 +799,28 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
                     queued = true;
                 }
             }
+        }
+        {
+            const uint64_t m = __builtin_amdgcn_ballot_w64(queued);
             if (queued) {
-                const uint32_t slot = atomicAdd(&qn[h], 1u); // < kQueueHalf, see below
-                queue[h][slot] = blk;
+                const uint32_t below = __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
+                                                                 __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+                queue[wv][wq + below] = blk;
             }
+            wq += (uint32_t)__builtin_popcountll(m);
         }
         if constexpr (WMSE) {
             col += col_step;
             col = col >= blocks_per_row ? col - blocks_per_row : col;
         }
-        __syncthreads();
-        // qn[h] cannot change before every thread has passed the next
-        // iteration's barrier, so all threads read the same count here.  At
-        // most kThreads entries join a half per use: drain it before overflow.
-        if (qn[h] > (uint32_t)(kQueueHalf - kThreads))
-            drain(h);
+        if (wq > 64u) {
+            wave_sync();
+            drain(wq);
+            wq = 0;
+        }
     }
-    __syncthreads();
-    drain(0);
-    drain(1);
+    wave_sync();
+    drain(wq);
 }
 
 // ---------------------------------------------------------------------------
