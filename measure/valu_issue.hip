@@ -1,7 +1,11 @@
 // valu_issue.hip -- issue cost of the VALU instructions the quantizers are
 // built from, measured on the device this runs on, and of two that a cheaper
 // error estimate would need (a decode to packed f16 and a binary32 fma with
-// an f16 operand).
+// an f16 operand).  Binary32 fma, mul, add and sub issue at twice the rate of
+// most other VALU instructions on this chip (rounding, min/max, integer and
+// bit operations, f16), so one representative of that slower class each
+// (v_rndne_f32, v_min_f32, v_add_u32) is measured too, written as single
+// inline-asm instructions so that the compiler cannot fold the chains.
 //
 // Each kernel keeps eight independent dependency chains per lane and runs
 // eight waves per SIMD, so the SIMD always has an instruction ready and the
@@ -26,7 +30,7 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kChains = 8;
 
-enum Kind { kFma32, kMul32, kEncode, kDecodeXor, kXor, kFma64, kDecodeF16Xor, kFmaMix };
+enum Kind { kFma32, kMul32, kEncode, kDecodeXor, kXor, kFma64, kDecodeF16Xor, kFmaMix, kRndne32, kMin32, kAddU32 };
 
 typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 
@@ -72,6 +76,12 @@ __global__ __launch_bounds__(kThreads) void chains(uint32_t* __restrict__ out, u
                 u[i] ^= u[(i + 1) % kChains];
             if constexpr (KIND == kFma64)
                 d[i] = __builtin_fma(d[i], 0.999, 0.001);
+            if constexpr (KIND == kRndne32)
+                asm volatile("v_rndne_f32 %0, %0" : "+v"(f[i]));
+            if constexpr (KIND == kMin32)
+                asm volatile("v_min_f32 %0, %0, %1" : "+v"(f[i]) : "v"(g[i]));
+            if constexpr (KIND == kAddU32)
+                asm volatile("v_add_u32 %0, %0, %1" : "+v"(u[i]) : "v"(u[(i + 1) % kChains]));
         }
     }
     const uint64_t t1 = __builtin_amdgcn_s_memtime();
@@ -175,14 +185,19 @@ int main()
     const double f64 = cost<kFma64>(s, iters / 4, 20, 1.0);
     const double dhx = cost<kDecodeF16Xor>(s, iters, 20, 1.0);
     const double mix = cost<kFmaMix>(s, iters, 20, 1.0);
-    if (fma < 0.0 || mul < 0.0 || enc < 0.0 || dx < 0.0 || x < 0.0 || f64 < 0.0 || dhx < 0.0 || mix < 0.0)
+    const double rnd = cost<kRndne32>(s, iters, 20, 1.0);
+    const double mn = cost<kMin32>(s, iters, 20, 1.0);
+    const double au = cost<kAddU32>(s, iters, 20, 1.0);
+    if (fma < 0.0 || mul < 0.0 || enc < 0.0 || dx < 0.0 || x < 0.0 || f64 < 0.0 || dhx < 0.0 || mix < 0.0 ||
+        rnd < 0.0 || mn < 0.0 || au < 0.0)
         return 1;
     printf("{\"device\": \"%s\", \"simds\": %d, \"clock_ghz_fma32\": %.3f, \"clock_ghz_encode\": %.3f, "
            "\"cycles_per_wave64_instr\": {\"v_fma_f32\": %.3f, \"v_mul_f32\": %.3f, "
            "\"v_cvt_scalef32_pk_fp4_f32\": %.3f, \"v_cvt_scalef32_pk_f32_fp4\": %.3f, "
            "\"v_xor_b32\": %.3f, \"v_fma_f64\": %.3f, \"v_cvt_scalef32_pk_f16_fp4\": %.3f, "
-           "\"v_fma_mix_f32\": %.3f}}\n",
-           p.gcnArchName, s.simds, fma_clk * 1e-9, enc_clk * 1e-9, fma, mul, enc, dx - x, x, f64, dhx - x, mix);
+           "\"v_fma_mix_f32\": %.3f, \"v_rndne_f32\": %.3f, \"v_min_f32\": %.3f, \"v_add_u32\": %.3f}}\n",
+           p.gcnArchName, s.simds, fma_clk * 1e-9, enc_clk * 1e-9, fma, mul, enc, dx - x, x, f64, dhx - x, mix,
+           rnd, mn, au);
     (void)hipFree(s.out);
     (void)hipFree(s.clk);
     return 0;
