@@ -112,7 +112,9 @@ def measured_valu():
     if v is None:
         return None
     v["source"] = ("profiles/nvfp4_sweep_valu_counters.md (SQ_INSTS_VALU, SQ_ACTIVE_INST_VALU, "
-                   "SQ_INSTS_VALU_CVT, GRBM_GUI_ACTIVE)")
+                   "SQ_INSTS_VALU_CVT, SQ_INSTS_VALU_FMA_F32/MUL_F32/ADD_F32, GRBM_GUI_ACTIVE; "
+                   "issue capacity prices binary32 fma/mul/add, conversions and other VALU "
+                   "instructions at their measured costs)")
     return v
 
 
@@ -194,14 +196,14 @@ def to_dev(x, dev):
 SETTLE_MS = 30.0  # GPU time of untimed calls before a secondary timing (clock settling)
 
 
-def event_time(fn, steps, warmup, settle_ms=0.0):
+def event_time(fn, steps, warmup, settle_ms=0.0, exact=False):
     """Average ms per call of fn(i) over `steps` calls, HIP events on the
     current stream (the stream every library call is issued on).  `warmup`
     untimed calls come first; with settle_ms > 0, more untimed calls follow
     until about that much GPU time has run, so that a short workload timed
     after an idle stretch (input generation on the host) is not measured
-    while the core clock is still rising, and at least settle_ms / 3 of calls
-    are timed."""
+    while the core clock is still rising, and unless `exact` at least
+    settle_ms / 3 of calls are timed (`exact` times exactly `steps`)."""
     import torch
     for i in range(warmup):
         fn(i)
@@ -219,7 +221,8 @@ def event_time(fn, steps, warmup, settle_ms=0.0):
         torch.cuda.synchronize()
         # and a timed region of at least a third of that, so that a short
         # workload is not timed over a fraction of a millisecond
-        steps = max(steps, int(settle_ms / 3 / per) + 1)
+        if not exact:
+            steps = max(steps, int(settle_ms / 3 / per) + 1)
     s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
     s.record()
@@ -501,13 +504,13 @@ def main():
 
     # `warmup` untimed steps, then about SETTLE_MS more of GPU time, so that
     # the core clock has settled before the timed steps
-    ms, wall = event_time(step, args.steps, args.warmup, SETTLE_MS)
+    ms, wall = event_time(step, args.steps, args.warmup, SETTLE_MS, exact=True)
     log(f"full call: {ms:.4f} ms/step (wall {wall:.3f}s)")
 
     def sweep_only(i):  # S supplied (the S of the full call): only the sweep kernel runs
         B.fp4q_quantize(spec_given, kv, None, codes, scales, gs, ws)
 
-    ms_k, _ = event_time(sweep_only, args.steps, args.warmup, SETTLE_MS)
+    ms_k, _ = event_time(sweep_only, args.steps, args.warmup, SETTLE_MS, exact=True)
     log(f"sweep kernel alone: {ms_k:.4f} ms, "
         f"{n * KV_BYTES_PER_ELEM_KERNEL / (ms_k * 1e-3) / 1e9:.0f} GB/s")
 
