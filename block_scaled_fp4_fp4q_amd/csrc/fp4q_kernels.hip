@@ -1833,9 +1833,13 @@ __device__ __forceinline__ float fpn_round(float y, uint32_t& code)
         code = q < 1.0f ? (uint32_t)(q * 8.0f) : ((((u >> 23) - 126u) << 3) | ((u >> 20) & 7u));
         return q;
     } else {
-        // E2M0 {0, 1, 2, 4}: the midpoints 0.5, 1.5 and 3 go to the even codes 0, 2, 2
-        code = y <= 0.5f ? 0u : (y < 1.5f ? 1u : (y <= 3.0f ? 2u : 3u));
-        return code == 3u ? 4.0f : (float)code;
+        // E2M0 {0, 1, 2, 4}, the midpoints 0.5, 1.5 and 3 going to the even
+        // codes 0, 2, 2: up to 3 that is min(RNE(y), 2) (adding 2^23 makes the
+        // binary32 ulp 1), above 3 it is 4
+        const float q = __builtin_fminf((y + 0x1p23f) - 0x1p23f, 2.0f);
+        const bool top = y > 3.0f;
+        code = top ? 3u : (uint32_t)q;
+        return top ? 4.0f : q;
     }
 }
 
@@ -1891,6 +1895,120 @@ __device__ __forceinline__ double intn_error16(const float* v, const float* w, f
     return E;
 }
 
+// gfx950's FP6 conversions.  v_cvt_scalef32_2xpk16_fp6_f32 (scale 1) rounds
+// 32 binary32 values to E2M3 exactly as IF6's FP grid does here (nearest,
+// ties to the even code, saturating at 7.5, the sign kept; an in-bounds
+// probe matched the exact rounding at every midpoint +-1 ulp, on the grid,
+// far beyond 7.5 and on signed zeros) and packs the 6-bit codes least
+// significant first, value j of its first operand in field 2j and value j of
+// its second in field 2j + 1; v_cvt_scalef32_pk32_f32_fp6 decodes the 32
+// fields in order.  So elements 2j and 2j + 1 of a block go to value j of
+// the two operands, and fields 0..15 -- the first three words -- are the
+// block's IF6 FP codes in the stored layout.  Values 8..15 of both operands
+// are unspecified padding whose codes are ignored.
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x32 __attribute__((ext_vector_type(32)));
+typedef uint32_t u32x6 __attribute__((ext_vector_type(6)));
+
+__device__ __forceinline__ u32x6 fp6_encode16(const float* v, float r, f32x16& a, f32x16& b)
+{
+    a = __builtin_nondeterministic_value(a);
+    b = __builtin_nondeterministic_value(b);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        a[j] = v[2 * j] * r;
+        b[j] = v[2 * j + 1] * r;
+    }
+    return __builtin_amdgcn_cvt_scalef32_2xpk16_fp6_f32(a, b, 1.0f);
+}
+
+// IF6's FP estimate through the hardware rounding: y = fl(v r) (signed, the
+// same magnitude as fl(|x| r)), q its decoded E2M3 value, d = y - q
+template <bool WMSE>
+__device__ __forceinline__ float fp6_est16(const float* v, const float* bw, float r)
+{
+    f32x16 a, b;
+    const u32x6 c = fp6_encode16(v, r, a, b);
+    const f32x32 q = __builtin_amdgcn_cvt_scalef32_pk32_f32_fp6(c, 1.0f);
+    float F = 0.0f;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+        float d = ((e & 1) ? b[e / 2] : a[e / 2]) - q[e];
+        if constexpr (WMSE)
+            d = bw[e] * d;
+        F = __builtin_fmaf(d, d, F);
+    }
+    return F;
+}
+
+// binary32 estimate of the FP grid's block error in units of D^2, from the
+// method's own codes (the FP rounding of fl(|x| r)): d = y - q, with weights
+// b d (b = sqrt(w)).  Same per-element error terms as the FP4 estimate.
+template <int N, bool WMSE>
+__device__ __forceinline__ float fpn_est16(const float* v, const float* b, float r)
+{
+    float F = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        uint32_t m;
+        const float y = __builtin_fabsf(v[i]) * r;
+        float d = y - fpn_round<N>(y, m);
+        if constexpr (WMSE)
+            d = b[i] * d;
+        F = __builtin_fmaf(d, d, F);
+    }
+    return F;
+}
+
+// the INT grid's estimate in units of D_int^2: t = fl(|x| ri + 1.5 2^23)
+// holds the exact product rounded to the nearest integer, saturated at
+// INTmax, q = t - 1.5 2^23, d = fl(|x| ri - q) with one rounding (q differs
+// from the method's only where fl(|x| ri) is a tie; |d| then moves by less
+// than one rounding of the product).  An infinite ri (D_int below 2^-128)
+// gives NaN or +inf, which the caller treats as undecided.
+template <int N, bool WMSE>
+__device__ __forceinline__ float intn_est16(const float* v, const float* b, float ri)
+{
+    constexpr float M = 12582912.0f;
+    float F = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        const float a = __builtin_fabsf(v[i]);
+        const float t = __builtin_fminf(__builtin_fmaf(a, ri, M), M + (float)IfnFormat<N>::kTop);
+        float d = __builtin_fmaf(a, ri, -(t - M));
+        if constexpr (WMSE)
+            d = b[i] * d;
+        F = __builtin_fmaf(d, d, F);
+    }
+    return F;
+}
+
+// the method's n-bit codes of the block on the FP grid (reciprocal r) or the
+// INT grid (reciprocal ri)
+template <int N>
+__device__ __forceinline__ void fpn_codes16(const float* v, float r, uint32_t* codes)
+{
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        uint32_t m;
+        fpn_round<N>(__builtin_fabsf(v[i]) * r, m);
+        codes[i] = ((__float_as_uint(v[i]) >> 31) << (N - 1)) | m;
+    }
+}
+
+template <int N>
+__device__ __forceinline__ void intn_codes16(const float* v, float ri, uint32_t* codes)
+{
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        const float a = __builtin_fabsf(v[i]);
+        const float q = a == 0.0f ? 0.0f
+                                  : __builtin_fminf(__builtin_rintf(a * ri), (float)IfnFormat<N>::kTop);
+        const int sq = (__float_as_uint(v[i]) >> 31) ? -(int)q : (int)q;
+        codes[i] = (uint32_t)sq & ((1u << N) - 1u);
+    }
+}
+
 // the block's 16 n-bit codes as 32-bit words, code i at bits n i .. n i + n - 1
 template <int N>
 __device__ __forceinline__ void pack_ifn(const uint32_t* c, uint32_t* w)
@@ -1939,8 +2057,12 @@ __global__ __launch_bounds__(kThreads) void ifn_quant(
     float* __restrict__ Sp, int lo, int hi, uint8_t* __restrict__ codes, uint8_t* __restrict__ scales)
 {
     using F = IfnFormat<N>;
-    // per pattern: D = fl32(s S), r = fl32(1/D), D_int = fl32(D step), r_int
+    // per pattern: D = fl32(s S), r = fl32(1/D), D_int = fl32(D step), r_int,
+    // and the estimates' units over S^2: s^2 and (s step)^2
     __shared__ float4 tab[128];
+    __shared__ float2 units[128];
+    __shared__ __attribute__((aligned(16))) float root[WMSE ? kRootCols : 1]; // read as float4
+    __shared__ float wsum[WMSE ? kRootCols / 16 : 1];
     float S;
     if (npart == 0) {
         S = *Sp;
@@ -1965,12 +2087,20 @@ __global__ __launch_bounds__(kThreads) void ifn_quant(
     }
     const float step = ifn_step<N>();
     for (int c = threadIdx.x; c < 128; c += kThreads) {
-        const float D = e4m3_value((uint32_t)(c < 0x7E ? c : 0x7E)) * S;
+        const float sv = e4m3_value((uint32_t)(c < 0x7E ? c : 0x7E));
+        const float D = sv * S;
         const float Di = D * step;
         tab[c] = make_float4(D, 1.0f / D, Di, 1.0f / Di);
+        const float sz = sv * step;
+        units[c] = make_float2(sv * sv, sz * sz);
     }
+    bool roots_in_lds = false;
+    if constexpr (WMSE)
+        roots_in_lds = roots_prologue(imp, blocks_per_row * 16, root, wsum);
     __syncthreads();
     const float SM = F::kFpMax * S;
+    const float invS = 1.0f / S;
+    constexpr float u = 0x1p-24f;
     for (int64_t blk = (int64_t)blockIdx.x * kThreads + threadIdx.x; blk < nblocks;
          blk += (int64_t)gridDim.x * kThreads) {
         float v[16];
@@ -1985,12 +2115,20 @@ __global__ __launch_bounds__(kThreads) void ifn_quant(
             for (int i = 0; i < 16; ++i)
                 cds[i] = (__float_as_uint(v[i]) >> 31) << (N - 1);
         } else {
-            float w[16];
-            if constexpr (WMSE)
-                load_weights16(imp, (blk % blocks_per_row) * 16, w);
+            const int64_t col0 = (blk % blocks_per_row) * 16;
             uint32_t sb = e4m3_round(a / SM);
             sb = sb < 1u ? 1u : sb;
-            double best = __builtin_huge_val();
+            // binary32 estimates of every (pattern, grid) in the method's
+            // order, in units of S^2, certified by the bound of the FP4
+            // estimates (A bounds |x| / S and FPmax D / S over the window;
+            // 40u covers the units (s fl(step))^2 against fl(fl(s S) step)^2)
+            float b[16];
+            float W = 16.0f;
+            if constexpr (WMSE)
+                block_roots<16>(imp, root, wsum, roots_in_lds, col0, b, W);
+            float e1 = __builtin_huge_valf(), e2 = __builtin_huge_valf();
+            int cb = (int)sb;
+            bool defined = true;
             int prev = -1;
             for (int k = lo; k <= hi; ++k) {
                 const int c = clamp_pattern((int)sb + k);
@@ -1998,22 +2136,71 @@ __global__ __launch_bounds__(kThreads) void ifn_quant(
                     continue;
                 prev = c;
                 const float4 t = tab[c];
-                const double ef = fpn_error16<N, WMSE>(v, w, t.x, t.y, nullptr);
-                if (ef < best) {
-                    best = ef;
-                    sbyte = (uint32_t)c;
-                }
-                const double ei = intn_error16<N, WMSE>(v, w, t.z, t.w, nullptr);
-                if (ei < best) {
-                    best = ei;
-                    sbyte = (uint32_t)c | 0x80u;
+                const float2 un = units[c];
+                float Ef;
+                if constexpr (N == 6)
+                    Ef = fp6_est16<WMSE>(v, b, t.y) * un.x;
+                else
+                    Ef = fpn_est16<N, WMSE>(v, b, t.y) * un.x;
+                const float Ei = intn_est16<N, WMSE>(v, b, t.w) * un.y;
+                // a NaN or infinite estimate (an infinite r_int, or |x| r
+                // overflowing) leaves the block to the exact search
+                defined = defined && Ef < __builtin_huge_valf() && Ei < __builtin_huge_valf();
+                keep_best(Ef, c, e1, e2, cb);
+                keep_best(Ei, c | 0x80, e1, e2, cb);
+            }
+            const int ctop = clamp_pattern((int)sb + hi);
+            const float A = __builtin_fmaxf(a * invS * (1.0f + 4.0f * u),
+                                            F::kFpMax * e4m3_value((uint32_t)ctop)) * (1.0f + 4.0f * u);
+            const float t1 = est_bound(e1, A, W, 40.0f * u), t2 = est_bound(e2, A, W, 40.0f * u);
+            const float4 tt = tab[ctop];
+            const bool finite = F::kFpMax * tt.x < __builtin_huge_valf() &&
+                                (float)F::kTop * tt.z < __builtin_huge_valf();
+            const bool certain = defined && finite && e1 < __builtin_huge_valf() &&
+                                 (e2 == __builtin_huge_valf() || e2 - t2 > e1 + t1);
+            if (certain) {
+                sbyte = (uint32_t)cb;
+            } else { // exact binary64 search (rare)
+                float w[16];
+                if constexpr (WMSE)
+                    load_weights16(imp, col0, w);
+                double best = __builtin_huge_val();
+                prev = -1;
+                for (int k = lo; k <= hi; ++k) {
+                    const int c = clamp_pattern((int)sb + k);
+                    if (c == prev)
+                        continue;
+                    prev = c;
+                    const float4 t = tab[c];
+                    const double ef = fpn_error16<N, WMSE>(v, w, t.x, t.y, nullptr);
+                    if (ef < best) {
+                        best = ef;
+                        sbyte = (uint32_t)c;
+                    }
+                    const double ei = intn_error16<N, WMSE>(v, w, t.z, t.w, nullptr);
+                    if (ei < best) {
+                        best = ei;
+                        sbyte = (uint32_t)c | 0x80u;
+                    }
                 }
             }
             const float4 t = tab[sbyte & 0x7Fu];
+            if constexpr (N == 6) {
+                if (!(sbyte & 0x80u)) {
+                    f32x16 pa, pb;
+                    const u32x6 c6 = fp6_encode16(v, t.y, pa, pb);
+                    words[0] = c6[0];
+                    words[1] = c6[1];
+                    words[2] = c6[2];
+                    store_ifn<N>(codes, blk, words);
+                    scales[blk] = (uint8_t)sbyte;
+                    continue;
+                }
+            }
             if (sbyte & 0x80u)
-                intn_error16<N, WMSE>(v, w, t.z, t.w, cds);
+                intn_codes16<N>(v, t.w, cds);
             else
-                fpn_error16<N, WMSE>(v, w, t.x, t.y, cds);
+                fpn_codes16<N>(v, t.y, cds);
         }
         pack_ifn<N>(cds, words);
         store_ifn<N>(codes, blk, words);

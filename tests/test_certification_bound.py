@@ -372,3 +372,73 @@ def test_bound_mxfp4_window(ref, mse):
         ex = t.sum(1) / np.ldexp(1.0, 2 * el)
         worst = max(worst, float((np.abs(ex - E) / bound(E, A, W, 32 * U)).max()))
     assert worst <= 1.0
+
+
+def fpn_grid_round(n, y):
+    """The method's FP rounding of binary32 y >= 0 for the n-bit type (the
+    oracle's own scalar routine, applied element-wise)."""
+    L = __import__("oracle.ref", fromlist=["lib"]).lib()
+    codes = np.vectorize(lambda t: L.fp4q_ref_fpn_round(n, f32(t)))(y)
+    return np.vectorize(lambda m: L.fp4q_ref_fpn_value(n, int(m)))(codes).astype(f32)
+
+
+def ifn_estimates(ref, n, v, w, S, c, mse):
+    """The IF3/IF6 kernel's binary32 estimates at pattern c, in units of S^2:
+    FP d = fl(y - q) from y = fl(|x| r); INT through 1.5 2^23 (RNE of the
+    exact product, saturated at INTmax), d = fl(|x| r_int - q)."""
+    L = ref.lib()
+    step = f32(L.fp4q_ref_ifn_step(n))
+    top = float((1 << (n - 1)) - 1)
+    s = E4M3[c]
+    D = (s * f32(S)).astype(f32)
+    r = (f32(1) / D).astype(f32)
+    Di = (D * step).astype(f32)
+    ri = (f32(1) / Di).astype(f32)
+    b = np.sqrt(w).astype(f32)
+    y = (np.abs(v) * r[:, None]).astype(f32)
+    dfp = (y - fpn_grid_round(n, y)).astype(f32)
+    p = np.abs(v).astype(f64) * ri.astype(f64)[:, None]
+    dint = (p - np.minimum(np.rint(p), top)).astype(f32)
+    out = []
+    for d, unit in ((dfp, (s * s).astype(f32)), (dint, ((s * step).astype(f32) ** 2).astype(f32))):
+        F = np.zeros(v.shape[0], f32)
+        for i in range(16):
+            e = d[:, i] if mse else (b[:, i] * d[:, i]).astype(f32)
+            F = fma32(e, e, F)
+        out.append((F * unit).astype(f32).astype(f64))
+    return out
+
+
+@pytest.mark.parametrize("n", [3, 6])
+@pytest.mark.parametrize("mse", [True, False])
+def test_bound_ifn_estimates(ref, n, mse):
+    # IF3 / IF6: the kernel's FP and INT estimates over a window against the
+    # oracle's binary64 errors of the same codes, with the 40u relative term
+    L = ref.lib()
+    rng = np.random.default_rng(30 + n)
+    v = np.concatenate([rng.uniform(-1, 1, (200, 16)), student(200, 31, scale=0.1)]).astype(np.float32)
+    v[::17] *= np.float32(1e-3)                       # blocks far below the tensor maximum
+    w = rng.lognormal(0, 2, v.shape).astype(np.float32)
+    fpmax = float(L.fp4q_ref_fpn_max(n))
+    S = L.fp4q_ref_ifn_global_scale(n, f32(np.abs(v).max()))
+    a = np.abs(v).max(1)
+    sb = np.array([max(1, L.fp4q_ref_ifn_base_scale(n, v[i].ctypes.data, 16, f32(S))) for i in range(len(v))])
+    W = np.full(len(v), 16.0)
+    if not mse:
+        Wf = np.zeros(len(v), f32)
+        for i in range(16):
+            Wf = (Wf + w[:, i]).astype(f32)
+        W = Wf.astype(f64)
+    worst = 0.0
+    for k in range(-3, 8):
+        c = np.clip(sb + k, 1, 0x7E)
+        ctop = np.clip(sb + 7, 1, 0x7E)
+        A = np.maximum(a.astype(f64) * f64(f32(1) / f32(S)) * (1 + 4 * U),
+                       fpmax * E4M3[ctop].astype(f64)) * (1 + 4 * U)
+        Ef, Ei = ifn_estimates(ref, n, v, w, S, c, mse)
+        exf = np.array([ref.fpn_block(n, v[i], S, int(c[i]), None if mse else w[i])[0] for i in range(len(v))])
+        exi = np.array([ref.intn_block(n, v[i], S, int(c[i]), None if mse else w[i])[0] for i in range(len(v))])
+        for E, ex in ((Ef, exf), (Ei, exi)):
+            ex = ex / (f64(S) * f64(S))
+            worst = max(worst, float((np.abs(ex - E) / bound(E, A, W, 40 * U)).max()))
+    assert worst <= 1.0

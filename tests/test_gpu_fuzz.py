@@ -53,9 +53,9 @@ def values(rng, rows, cols, block):
     return np.where(zero, 0.0, x).astype(np.float32), kind
 
 
-def draw(seed, B):
+def draw(seed, B, fmts=("nvfp4", "mxfp4", "if4")):
     rng = np.random.default_rng(seed)
-    fmt = ["nvfp4", "mxfp4", "if4"][int(rng.integers(0, 3))]
+    fmt = fmts[int(rng.integers(0, len(fmts)))]
     block = 32 if fmt == "mxfp4" else 16
     rules = [B.FP4Q_SCALE_ABSMAX, B.FP4Q_SCALE_SWEEP] + ([B.FP4Q_SCALE_FOUR_OVER_SIX] if fmt == "nvfp4" else [])
     rule = rules[int(rng.integers(0, len(rules)))]
@@ -89,11 +89,26 @@ def draw(seed, B):
                 x=synth.f32_to_bf16_bits(x) if bf16 else x, imp=imp, given=given, kind=kind)
 
 
+def formats(B, ref):
+    return ({"nvfp4": B.FP4Q_NVFP4, "mxfp4": B.FP4Q_MXFP4, "if4": B.FP4Q_IF4, "if3": B.FP4Q_IF3,
+             "if6": B.FP4Q_IF6},
+            {"nvfp4": ref.NVFP4, "mxfp4": ref.MXFP4, "if4": ref.IF4, "if3": ref.IF3, "if6": ref.IF6})
+
+
 @pytest.mark.parametrize("case", range(CASES))
 def test_random_configuration(B, ref, case):
-    c = draw(1000 + case, B)
-    bfmt = {"nvfp4": B.FP4Q_NVFP4, "mxfp4": B.FP4Q_MXFP4, "if4": B.FP4Q_IF4}[c["fmt"]]
-    ofmt = {"nvfp4": ref.NVFP4, "mxfp4": ref.MXFP4, "if4": ref.IF4}[c["fmt"]]
+    check_case(B, ref, case, draw(1000 + case, B))
+
+
+@pytest.mark.parametrize("case", range(300))
+def test_random_adaptive(B, ref, case):
+    """IF3 and IF6 (AbsMax and pattern windows) drawn the same way."""
+    check_case(B, ref, case, draw(7000 + case, B, fmts=("if3", "if6")))
+
+
+def check_case(B, ref, case, c):
+    bfmts, ofmts = formats(B, ref)
+    bfmt, ofmt = bfmts[c["fmt"]], ofmts[c["fmt"]]
     x, imp, wmse = c["x"], c["imp"], c["objective"] == 1
     print(f"case {case}: {c['fmt']} rule {c['rule']} objective {c['objective']} rotate {c['rotate']} "
           f"window {c['window']} shape {x.shape} {x.dtype} kind {c['kind']} given {c['given']}", flush=True)
