@@ -196,20 +196,25 @@ __device__ __forceinline__ double int4_error16(const float* v, const float* w, f
 __device__ __forceinline__ uint2 encode16_int4(const float* v, float ri)
 {
     // RNE is odd-symmetric, so clamping rint(v ri) to [-7, 7] gives
-    // sign(v) min(RNE(|v| ri), 7); its low four bits are the two's complement
-    // nibble (a signed zero gives 0)
-    uint32_t lo = 0, hi = 0;
+    // sign(v) min(RNE(|v| ri), 7) (a signed zero gives 0).  q + 8, in [1, 15],
+    // goes to byte k of ev (element 8h + 2k) or od (element 8h + 2k + 1) by a
+    // byte conversion; byte k of ev | od << 4 then holds elements 2k and
+    // 2k + 1, and (q + 8) XOR 8 is q's two's complement nibble
+    uint32_t out[2];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-        const float t = __builtin_rintf(v[i] * ri);
-        const int q = (int)__builtin_fmaxf(__builtin_fminf(t, 7.0f), -7.0f);
-        const uint32_t nib = (uint32_t)q & 0xFu;
-        if (i < 8)
-            lo |= nib << (4 * i);
-        else
-            hi |= nib << (4 * (i - 8));
+    for (int h = 0; h < 2; ++h) {
+        uint32_t ev = __builtin_nondeterministic_value(0u), od = __builtin_nondeterministic_value(0u);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) { // every byte of ev and od is written
+            const float q = __builtin_amdgcn_fmed3f(__builtin_rintf(v[8 * h + j] * ri), -7.0f, 7.0f);
+            if (j & 1)
+                od = __builtin_amdgcn_cvt_pk_u8_f32(q + 8.0f, j / 2, od);
+            else
+                ev = __builtin_amdgcn_cvt_pk_u8_f32(q + 8.0f, j / 2, ev);
+        }
+        out[h] = (ev | (od << 4)) ^ 0x88888888u;
     }
-    return make_uint2(lo, hi);
+    return make_uint2(out[0], out[1]);
 }
 
 // fp4_error16 and int4_error16 (MSE) of one block together, element by
