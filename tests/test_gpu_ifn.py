@@ -152,3 +152,19 @@ def test_full_if4_workload(B, ref, fmt):
     xd, codes, scales, gs, want = run(B, ref, fmt, x)
     ind = (scales.cpu().numpy() & 0x80) != 0
     print(f"{fmt}: INT share uniform {ind[uniform].mean():.3f}, spiky {ind[~uniform].mean():.3f}")
+
+
+@pytest.mark.parametrize("fmt", ["if3", "if6"])
+def test_int_step_below_2_pow_128(B, ref, fmt):
+    # under the smallest global scale, blocks whose maximum is about 2^-123
+    # land on pattern 0x01 (D = 2^-126); IF6's INT step is then below 2^-128,
+    # its reciprocal +inf, and zero elements must still get q = 0 (the
+    # kernels' estimates turn NaN or infinite there and the exact search
+    # decides).  Zeros, signed zeros and values across the low patterns.
+    rng = np.random.default_rng(77)
+    x = (rng.uniform(-1, 1, (8, 64)) * 2.0 ** -123).astype(np.float32)
+    x[:, ::5] = 0.0
+    x[:, 1::7] = -0.0
+    x[3] *= np.float32(64.0)                 # a few patterns higher
+    for window in (None, (-3, 7), (-126, 126)):
+        run(B, ref, fmt, x, rule=0 if window is None else 1, window=window, given=2.0 ** -117)
