@@ -453,24 +453,32 @@ __device__ __forceinline__ void fp4_err32(const float* v, const float* b, float 
         for (int j = 0; j < 8; ++j)
             y[j] = v[8 * g + j] * r;
         uint32_t c = fresh_word(y[0]), c2 = fresh_word(y[1]);
+        // the half block's conversions are issued as one group, between
+        // scheduling barriers: interleaving FP4 conversions with binary32
+        // arithmetic costs more issue cycles than grouping them (measured:
+        // the KV sweep 3.5% and the c2 sweep 4.6% faster grouped)
+        __builtin_amdgcn_sched_barrier(0);
         c = fp4_pack2<0>(c, y[0], y[1]);
         c = fp4_pack2<1>(c, y[2], y[3]);
         c = fp4_pack2<2>(c, y[4], y[5]);
         c = fp4_pack2<3>(c, y[6], y[7]);
-        fp4_unpack2<0>(c, q[0], q[1]);
-        fp4_unpack2<1>(c, q[2], q[3]);
-        fp4_unpack2<2>(c, q[4], q[5]);
-        fp4_unpack2<3>(c, q[6], q[7]);
         if constexpr (PAIR) {
             c2 = fp4_pack2_scaled<0>(c2, y[0], y[1], 2.0f);
             c2 = fp4_pack2_scaled<1>(c2, y[2], y[3], 2.0f);
             c2 = fp4_pack2_scaled<2>(c2, y[4], y[5], 2.0f);
             c2 = fp4_pack2_scaled<3>(c2, y[6], y[7], 2.0f);
+        }
+        fp4_unpack2<0>(c, q[0], q[1]);
+        fp4_unpack2<1>(c, q[2], q[3]);
+        fp4_unpack2<2>(c, q[4], q[5]);
+        fp4_unpack2<3>(c, q[6], q[7]);
+        if constexpr (PAIR) {
             fp4_unpack2_scaled<0>(c2, h[0], h[1], 2.0f);
             fp4_unpack2_scaled<1>(c2, h[2], h[3], 2.0f);
             fp4_unpack2_scaled<2>(c2, h[4], h[5], 2.0f);
             fp4_unpack2_scaled<3>(c2, h[6], h[7], 2.0f);
         }
+        __builtin_amdgcn_sched_barrier(0);
         if (words)
             words[g] = c;
 #pragma unroll
