@@ -25,7 +25,7 @@
 namespace fp4q {
 
 constexpr int kThreads = 256;
-constexpr int kAmaxGroups = 1024; // partial maxima per call (<= kMaxPartials)
+constexpr int kAmaxGroups = 1024; // partial maxima per call (4 KiB of the 32 KiB workspace)
 
 // ---------------------------------------------------------------------------
 // global maximum
@@ -529,13 +529,22 @@ __device__ __forceinline__ void keep_best_packed(float E, uint32_t k, uint32_t& 
     p1 = p1 < p ? p1 : p;
 }
 
+// one pattern's constants: the pair every candidate reads (r, s*s) first,
+// so that it is one aligned 8-byte LDS load with an immediate offset
+struct alignas(16) SweepPattern {
+    float r;    // fl32(1/D)
+    float s2;   // s*s, exact
+    float D;    // fl32(s S)
+    float pair; // 1 when the pattern eight steps up has exactly twice this step
+};
+
 // the whole window [LO, HI] known at compile time, every pattern sb+k normal
 // and finite, and every pair (k, k+8) an exact doubling: fully unrolled, no
 // clamps or masks.  Returns the two least packed estimates (see above); only
 // a strict gap beyond the error bounds is certified, so the order among
 // near-equal estimates never decides a result.
 template <bool WMSE, int LO, int HI>
-__device__ __forceinline__ void sweep_fixed(const float* v, const float* b, const float4* tab, int sb,
+__device__ __forceinline__ void sweep_fixed(const float* v, const float* b, const SweepPattern* tab, int sb,
                                             uint32_t& p1, uint32_t& p2)
 {
     static_assert(HI - LO < 16, "the window offset must fit in four bits");
@@ -543,15 +552,15 @@ __device__ __forceinline__ void sweep_fixed(const float* v, const float* b, cons
     for (int k = LO; k <= HI; ++k) {
         if (((k - LO) & 15) >= 8)
             continue; // evaluated with its partner k-8
-        const float4 t = tab[sb + k];
+        const SweepPattern t = tab[sb + k];
         float F1, F2;
         if (k + 8 <= HI) {
-            fp4_err32<WMSE, true>(v, b, t.y, F1, F2);
-            keep_best_packed(F1 * t.z, (uint32_t)(k - LO), p1, p2);
-            keep_best_packed(F2 * t.z, (uint32_t)(k + 8 - LO), p1, p2);
+            fp4_err32<WMSE, true>(v, b, t.r, F1, F2);
+            keep_best_packed(F1 * t.s2, (uint32_t)(k - LO), p1, p2);
+            keep_best_packed(F2 * t.s2, (uint32_t)(k + 8 - LO), p1, p2);
         } else {
-            fp4_err32<WMSE, false>(v, b, t.y, F1, F2);
-            keep_best_packed(F1 * t.z, (uint32_t)(k - LO), p1, p2);
+            fp4_err32<WMSE, false>(v, b, t.r, F1, F2);
+            keep_best_packed(F1 * t.s2, (uint32_t)(k - LO), p1, p2);
         }
     }
 }
@@ -562,11 +571,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
     const float* __restrict__ imp, const float* __restrict__ partials, int npart,
     float* __restrict__ Sp, int lo, int hi, uint2* __restrict__ codes, uint8_t* __restrict__ scales)
 {
-    // per pattern: D = fl32(s S), r = fl32(1/D), s*s (exact), and 1 when the
+    // per pattern: r = fl32(1/D), s*s (exact), D = fl32(s S), and 1 when the
     // pattern eight steps up has exactly twice this step (so one product
     // serves both), else 0.  Estimates are kept in units of S^2: s*s is
     // normal for every pattern, while D*D would underflow for small S.
-    __shared__ float4 tab[128];
+    __shared__ SweepPattern tab[128];
     // uncertified blocks, one queue per wave: a wave appends at most 64 per
     // iteration and drains its queue once it holds more than 64
     __shared__ int64_t queue[kThreads / 64][128];
@@ -580,7 +589,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
         const float D = sc * S;
         const float D8 = e4m3_value((uint32_t)(c + 8 < 0x7E ? c + 8 : 0x7E)) * S;
         const bool twice = c >= 8 && c + 8 <= 0x7E && D8 == 2.0f * D && (1.0f / D8) == 0.5f * (1.0f / D);
-        tab[c] = make_float4(D, 1.0f / D, sc * sc, twice ? 1.0f : 0.0f);
+        tab[c] = SweepPattern{1.0f / D, sc * sc, D, twice ? 1.0f : 0.0f};
     }
     bool roots_in_lds = false;
     if constexpr (WMSE)
@@ -588,7 +597,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
     __syncthreads();
     // every pair (c, c+8) with c in [8, 0x76] an exact doubling (true unless S
     // pushes the steps to the ends of the binary32 range)
-    const bool pairs_exact = __syncthreads_and(threadIdx.x < 8 || threadIdx.x > 0x76 || tab[threadIdx.x].w != 0.0f);
+    const bool pairs_exact = __syncthreads_and(threadIdx.x < 8 || threadIdx.x > 0x76 || tab[threadIdx.x].pair != 0.0f);
     constexpr int FLO = WIN == 1 ? -3 : -8, FHI = 7;
     const float S6 = 6.0f * S;
     const float invS = 1.0f / S;
@@ -651,12 +660,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
             int cb = 0x7F;
             for (int k = lo + sub; k <= hi; k += 16) {
                 const int c = clamp_pattern((int)sb + k);
-                const float4 t = tab[c];
+                const SweepPattern t = tab[c];
                 double E = 0.0;
 #pragma unroll 1
                 for (int i = 0; i < 16; ++i) {
                     const float a = __builtin_fabsf(xs[i]);
-                    const float xh = e2m1_q(a * t.y) * t.x;
+                    const float xh = e2m1_q(a * t.r) * t.D;
                     const double d = (double)a - (double)xh;
                     double tt = d * d;
                     if constexpr (WMSE)
@@ -682,7 +691,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
 #pragma unroll
                 for (int i = 0; i < 16; ++i)
                     v[i] = xs[i];
-                codes[blk] = fp4_encode16(v, tab[cb].y);
+                codes[blk] = fp4_encode16(v, tab[cb].r);
                 scales[blk] = (uint8_t)cb;
             }
             wave_sync(); // the stage is rewritten next round
@@ -760,27 +769,27 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
                             continue; // evaluated with its partner k-8 (uniform branch)
                         const bool ok1 = k >= klo && k <= khi;
                         const int c = clamp_pattern((int)sb + k);
-                        const float4 t = tab[c];
+                        const SweepPattern t = tab[c];
                         if (k + 8 <= hi) {
                             const bool ok2 = k + 8 >= klo && k + 8 <= khi;
                             const int c8 = clamp_pattern((int)sb + k + 8);
                             float F1, F2, E2;
-                            if (__builtin_amdgcn_ballot_w64(t.w == 0.0f) == 0) {
+                            if (__builtin_amdgcn_ballot_w64(t.pair == 0.0f) == 0) {
                                 // every lane's pair is an exact doubling: shared product
-                                fp4_err32<WMSE, true>(v, b, t.y, F1, F2);
-                                E2 = F2 * t.z;
+                                fp4_err32<WMSE, true>(v, b, t.r, F1, F2);
+                                E2 = F2 * t.s2;
                             } else {
                                 float unused;
-                                fp4_err32<WMSE, false>(v, b, t.y, F1, unused);
-                                fp4_err32<WMSE, false>(v, b, tab[c8].y, F2, unused);
-                                E2 = F2 * tab[c8].z;
+                                fp4_err32<WMSE, false>(v, b, t.r, F1, unused);
+                                fp4_err32<WMSE, false>(v, b, tab[c8].r, F2, unused);
+                                E2 = F2 * tab[c8].s2;
                             }
-                            keep_best(ok1 ? F1 * t.z : __builtin_huge_valf(), c, e1, e2, cb);
+                            keep_best(ok1 ? F1 * t.s2 : __builtin_huge_valf(), c, e1, e2, cb);
                             keep_best(ok2 ? E2 : __builtin_huge_valf(), c8, e1, e2, cb);
                         } else {
                             float F1, unused;
-                            fp4_err32<WMSE, false>(v, b, t.y, F1, unused);
-                            keep_best(ok1 ? F1 * t.z : __builtin_huge_valf(), c, e1, e2, cb);
+                            fp4_err32<WMSE, false>(v, b, t.r, F1, unused);
+                            keep_best(ok1 ? F1 * t.s2 : __builtin_huge_valf(), c, e1, e2, cb);
                         }
                     }
                 }
@@ -802,11 +811,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
                 const float t2 = 16.0f * u * A * s2 + rel * e2 + tail;
                 // 6 D of the window's top pattern finite: no candidate's
                 // reconstruction overflows (the exact path handles those)
-                const bool finite_top = 6.0f * tab[clamp_pattern((int)sb + hi)].x < __builtin_huge_valf();
+                const bool finite_top = 6.0f * tab[clamp_pattern((int)sb + hi)].D < __builtin_huge_valf();
                 const bool certain = klo <= khi && finite_top && e1 < __builtin_huge_valf() &&
                                      ((e2 == __builtin_huge_valf()) || (e2 - t2 > e1 + t1));
                 if (certain) {
-                    codes[blk] = fp4_encode16(v, tab[cb].y);
+                    codes[blk] = fp4_encode16(v, tab[cb].r);
                     scales[blk] = (uint8_t)cb;
                 } else {
                     queued = true;
