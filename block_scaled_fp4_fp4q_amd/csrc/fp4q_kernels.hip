@@ -2012,22 +2012,47 @@ __device__ __forceinline__ void fpn_codes16(const float* v, float r, uint32_t* c
 {
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-        uint32_t m;
-        fpn_round<N>(__builtin_fabsf(v[i]) * r, m);
-        codes[i] = ((__float_as_uint(v[i]) >> 31) << (N - 1)) | m;
+        const uint32_t xb = __float_as_uint(v[i]);
+        const float y = __builtin_fabsf(v[i]) * r;
+        if constexpr (N == 3) {
+            // E2M0: t = fl(y + 2^23) - 2^23 is RNE(y); min(RNE(y), 2) is the
+            // code up to 3 and 3 (the value 4) above it, so the low two bits
+            // of t clamped to 2^23 + 2 (or 2^23 + 3 above 3) are the
+            // magnitude code; the sign goes to bit 2
+            const float t = y > 3.0f ? 0x1p23f + 3.0f : __builtin_fminf(y + 0x1p23f, 0x1p23f + 2.0f);
+            codes[i] = (__float_as_uint(t) & 3u) | ((xb >> 29) & ~3u); // xb >> 29 < 8
+        } else {
+            uint32_t m;
+            fpn_round<N>(y, m);
+            codes[i] = ((xb >> 31) << (N - 1)) | m;
+        }
     }
 }
 
+// INT codes are the n-bit two's complement of sign(x) min(RNE(fl(|x| ri)),
+// INTmax).  With a finite ri, t = fl(fl(x ri) + 1.5 2^23) holds that signed
+// integer plus 1.5 2^23 (the binary32 ulp there is 1, and rounding to nearest
+// even is symmetric about 1.5 2^23, which is even); clamped to 1.5 2^23 +-
+// INTmax, the low n bits of t are the code.  An infinite ri (D_int below
+// 2^-128) takes the plain form, where a zero element stays 0.
 template <int N>
 __device__ __forceinline__ void intn_codes16(const float* v, float ri, uint32_t* codes)
 {
+    constexpr float M = 12582912.0f, T = (float)IfnFormat<N>::kTop;
+    if (ri < __builtin_huge_valf()) {
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-        const float a = __builtin_fabsf(v[i]);
-        const float q = a == 0.0f ? 0.0f
-                                  : __builtin_fminf(__builtin_rintf(a * ri), (float)IfnFormat<N>::kTop);
-        const int sq = (__float_as_uint(v[i]) >> 31) ? -(int)q : (int)q;
-        codes[i] = (uint32_t)sq & ((1u << N) - 1u);
+        for (int i = 0; i < 16; ++i) {
+            const float t = __builtin_amdgcn_fmed3f(v[i] * ri + M, M - T, M + T);
+            codes[i] = __float_as_uint(t) & ((1u << N) - 1u);
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const float a = __builtin_fabsf(v[i]);
+            const float q = a == 0.0f ? 0.0f : T;
+            const int sq = (__float_as_uint(v[i]) >> 31) ? -(int)q : (int)q;
+            codes[i] = (uint32_t)sq & ((1u << N) - 1u);
+        }
     }
 }
 
