@@ -107,8 +107,7 @@ def test_mxfp4_wide_windows(B, ref, window):
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 def test_mxfp4_window_extremes(B, ref, dtype):
     # exponents clamped at both ends of E8M0, subnormal inputs, zero blocks,
-    # signed zeros and values that saturate (bf16 input runs four lanes per
-    # block, and the clamped windows its gathered exact search)
+    # signed zeros and values that saturate, on both input types
     rng = np.random.default_rng(53)
     x = rng.standard_normal((8, 128)).astype(np.float32)
     x[0] *= np.float32(2.0 ** -140)        # subnormal, OCP exponent below -127
