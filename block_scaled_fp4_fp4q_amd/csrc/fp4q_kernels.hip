@@ -321,34 +321,41 @@ __device__ __forceinline__ float est_bound(float E, float A, float W, float rel)
 
 // INT4 estimate of IF4's 6/7 method in units of the INT4 step, with q the
 // method's integer min(RNE(fl(|x| ri)), 7), also packing the method's INT4
-// nibbles: RNE is odd-symmetric, so q = clamp(rint(v ri), -7, 7) is
-// sign(v) min(RNE(|v| ri), 7), (v ri - q)^2 the same term, and the low four
-// bits of q its two's complement nibble
-template <bool WMSE>
+// nibbles.  z = fl(v ri) and t = fl(z + 1.5 2^23) = RNE(z) + 1.5 2^23 (the
+// binary32 ulp there is 1; rounding to nearest even is odd-symmetric, so
+// RNE(z) is sign(v) RNE(|v| ri)); CLAMP saturates t at +-7, which the caller
+// leaves out where |v| ri stays below 7.5.  Then q = t - 1.5 2^23, the term
+// (z - q)^2, and q + 8 = t - (1.5 2^23 - 8) in [1, 15] packed as bytes.
+template <bool WMSE, bool CLAMP>
 __device__ __forceinline__ float int4_est16_codes(const float* v, const float* b, float ri, uint2& words)
 {
+    constexpr float M = 12582912.0f;
     float F = 0.0f;
     uint32_t out[2];
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-        // q + 8, in [1, 15], as byte k of ev (element 8h + 2k) or od
-        // (element 8h + 2k + 1); every byte is written
+        // q + 8 as byte k of ev (element 8h + 2k) or od (element 8h + 2k + 1);
+        // every byte is written
         uint32_t ev = 0u, od = 0u;
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
             const int i = 8 * h + j;
             const float z = v[i] * ri;
-            const float q = __builtin_amdgcn_fmed3f(__builtin_rintf(z), -7.0f, 7.0f);
+            float t = z + M;
+            if constexpr (CLAMP)
+                t = __builtin_amdgcn_fmed3f(t, M - 7.0f, M + 7.0f);
+            const float q = t - M;
             float d;
             if constexpr (WMSE)
                 d = __builtin_fmaf(-b[i], q, b[i] * z);
             else
                 d = z - q;
             F = __builtin_fmaf(d, d, F);
+            const float q8 = t - (M - 8.0f);
             if (j & 1)
-                od = __builtin_amdgcn_cvt_pk_u8_f32(q + 8.0f, j / 2, od);
+                od = __builtin_amdgcn_cvt_pk_u8_f32(q8, j / 2, od);
             else
-                ev = __builtin_amdgcn_cvt_pk_u8_f32(q + 8.0f, j / 2, ev);
+                ev = __builtin_amdgcn_cvt_pk_u8_f32(q8, j / 2, ev);
         }
         // byte k of ev | od << 4 holds q + 8 of elements 2k (low nibble) and
         // 2k+1; (q + 8) XOR 8 is q mod 16, the two's complement nibble
@@ -909,8 +916,12 @@ __global__ __launch_bounds__(kThreads) void if4_quant(
             uint32_t cw[2];
             float Ff, unused;
             fp4_err32<WMSE, false>(v, b, r, Ff, unused, cw);
+            // at s_base |x| ri < 7 (17/16) < 7.5 unless s_base is subnormal
+            // or saturated (a given S)
             uint2 int4_words;
-            const float Fi = int4_est16_codes<WMSE>(v, b, ri, int4_words);
+            const float Fi = __builtin_amdgcn_ballot_w64(sb < 8u || sb >= 0x7Eu) != 0
+                                 ? int4_est16_codes<WMSE, true>(v, b, ri, int4_words)
+                                 : int4_est16_codes<WMSE, false>(v, b, ri, int4_words);
             const float sz = sv * kInt4Step;
             const float Ef = Ff * (sv * sv), Ei = Fi * (sz * sz);
             const float A = __builtin_fmaxf(a * invS * (1.0f + 4.0f * u), 6.0f * sv) * (1.0f + 4.0f * u);
