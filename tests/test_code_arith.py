@@ -1,0 +1,122 @@
+"""The kernels' integer-code shortcuts, pinned on the CPU against the plain
+statement of the codes.
+
+The quantize kernels do not round and convert element by element when they
+form INT codes; they add 1.5 2^23 to the binary32 product (the binary32 ulp
+there is 1, so the sum holds the product rounded to the nearest integer, ties
+to even, with the sign of x) and read the code from the sum's low mantissa
+bits.  Each test rebuilds one such sequence in numpy binary32 and compares it,
+element by element, with the method's definition written directly: the codes
+of the rounded product min(RNE(fl32(|x| r)), INTmax) with the sign of x.
+
+- IF3 / IF6 INT codes (Adaptive Block-Scaled Data Types, Methodology, at 3
+  and 6 bits under the reading stated in include/fp4q.h): the n-bit two's
+  complement of the signed integer.
+- IF4 INT4 nibbles (same page, Methodology): q + 8 as a byte, whose XOR with
+  8 is the two's complement nibble.
+- IF3 FP codes (E2M0, magnitudes {0, 1, 2, 4}): the magnitude code from the
+  same kind of sum, the sign in bit 2.
+"""
+import numpy as np
+import pytest
+
+f32 = np.float32
+M = f32(12582912.0)            # 1.5 2^23
+
+
+def products(seed, n=200_000):
+    """(x, r) pairs over the cases that matter: random magnitudes, exact
+    ties k + 1/2 of both signs, zeros of both signs, values far past the
+    saturation point, and tiny values."""
+    rng = np.random.default_rng(seed)
+    x = (rng.standard_normal(n) * np.exp2(rng.integers(-8, 8, n))).astype(f32)
+    r = np.exp2(rng.integers(-6, 7, n)).astype(f32) * f32(1.0) / f32(1.125) ** rng.integers(0, 8, n)
+    r = r.astype(f32)
+    # exact ties: x r = +-(k + 1/2) with r a power of two
+    k = rng.integers(0, 40, 4000)
+    e = rng.integers(-4, 5, 4000)
+    rt = np.exp2(e).astype(f32)
+    xt = ((k + 0.5) / rt * np.where(rng.integers(0, 2, 4000) == 1, 1, -1)).astype(f32)
+    # one binary32 step either side of those ties
+    xs = np.concatenate([xt, np.nextafter(xt, f32(np.inf)), np.nextafter(xt, f32(-np.inf))])
+    rs = np.concatenate([rt, rt, rt])
+    special = np.array([0.0, -0.0, 1e30, -1e30, 1e-30, -1e-30, 2.0 ** -149, -(2.0 ** -149)], f32)
+    x = np.concatenate([x, xs, special])
+    r = np.concatenate([r, rs, np.full(special.size, f32(0.75))])
+    return x.astype(f32), r.astype(f32)
+
+
+def plain_signed_int(x, r, top):
+    """sign(x) min(RNE(fl32(|x| r)), top) as int64 (the method's INT value)."""
+    y = (np.abs(x) * r).astype(f32)
+    q = np.minimum(np.rint(y.astype(np.float64)), top).astype(np.int64)
+    return np.where(np.signbit(x), -q, q)
+
+
+def magic_sum(x, r, top):
+    """fl32(fl32(x r) + 1.5 2^23) clamped to 1.5 2^23 +- top (one med3)."""
+    z = (x * r).astype(f32)
+    t = (z + M).astype(f32)
+    return np.clip(t, M - f32(top), M + f32(top)).astype(f32)
+
+
+@pytest.mark.parametrize("n", [3, 6])
+def test_ifn_int_codes(n):
+    top = (1 << (n - 1)) - 1
+    x, r = products(10 + n)
+    got = magic_sum(x, r, top).view(np.uint32) & np.uint32((1 << n) - 1)
+    want = (plain_signed_int(x, r, top) & ((1 << n) - 1)).astype(np.uint32)
+    bad = np.nonzero(got != want)[0]
+    assert bad.size == 0, (x[bad[:5]], r[bad[:5]], got[bad[:5]], want[bad[:5]])
+
+
+def test_if4_int4_nibbles():
+    x, r = products(14)
+    for clamp in (True, False):
+        if clamp:
+            t = magic_sum(x, r, 7)
+            xx, rr = x, r
+        else:
+            # the unclamped form is used only where |x| r stays below 7.5
+            keep = (np.abs(x) * r).astype(f32) < f32(7.5)
+            xx, rr = x[keep], r[keep]
+            t = ((xx * rr).astype(f32) + M).astype(f32)
+        q8 = (t - (M - f32(8))).astype(f32)          # q + 8, one byte each
+        assert np.all((q8 >= 1) & (q8 <= 15) & (q8 == np.floor(q8)))
+        nib = (q8.astype(np.uint32) ^ np.uint32(8)) & np.uint32(15)
+        want = (plain_signed_int(xx, rr, 7) & 15).astype(np.uint32)
+        assert np.array_equal(nib, want)
+        # and the term's q: t - 1.5 2^23 is the signed integer itself
+        assert np.array_equal((t - M).astype(np.int64), plain_signed_int(xx, rr, 7))
+
+
+def e2m0_plain(y):
+    """Magnitude code of the nearest of {0, 1, 2, 4} to y >= 0, ties to the
+    even code, saturating at 4 -- by exhaustive comparison in binary64."""
+    grid = np.array([0.0, 1.0, 2.0, 4.0])
+    d = np.abs(y.astype(np.float64)[:, None] - grid)
+    m = d.min(1, keepdims=True)
+    tie = d == m
+    even = tie & (np.arange(4) % 2 == 0)
+    k = np.where(even.any(1), even.argmax(1), tie.argmax(1))
+    # at and beyond 4 the nearest is 4 (and the binary64 distances above
+    # would round to ties for huge y)
+    return np.where(y >= 4, 3, k).astype(np.uint32)
+
+
+def test_if3_fp_codes():
+    x, r = products(15)
+    # midpoints 0.5, 1.5, 3 of the E2M0 grid and their neighbours as products
+    mids = np.array([0.5, 1.5, 3.0, 2.5, 3.5, 5.0], f32)
+    xm = np.concatenate([mids, np.nextafter(mids, f32(0)), np.nextafter(mids, f32(9))])
+    x = np.concatenate([x, xm, -xm])
+    r = np.concatenate([r, np.ones(2 * xm.size, f32)])
+    y = (np.abs(x) * r).astype(f32)
+    t = np.where(y > f32(3), f32(2.0 ** 23 + 3),
+                 np.minimum((y + f32(2.0 ** 23)).astype(f32), f32(2.0 ** 23) + f32(2)))
+    t = t.astype(f32)
+    xb = x.view(np.uint32)
+    got = (t.view(np.uint32) & np.uint32(3)) | ((xb >> np.uint32(29)) & ~np.uint32(3))
+    want = e2m0_plain(y) | (np.signbit(x).astype(np.uint32) << np.uint32(2))
+    bad = np.nonzero(got != want)[0]
+    assert bad.size == 0, (x[bad[:5]], y[bad[:5]], got[bad[:5]], want[bad[:5]])
