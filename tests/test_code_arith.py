@@ -120,3 +120,51 @@ def test_if3_fp_codes():
     want = e2m0_plain(y) | (np.signbit(x).astype(np.uint32) << np.uint32(2))
     bad = np.nonzero(got != want)[0]
     assert bad.size == 0, (x[bad[:5]], y[bad[:5]], got[bad[:5]], want[bad[:5]])
+
+
+def fpn_value_kernel(n, y):
+    """The kernels' FP rounding of y >= 0 through magic constants: E2M3
+    adds 2^20 / 2^21 / 2^22 below 2 / 4 / above (the binary32 ulp there is the
+    E2M3 step) and saturates at 7.5; E2M0 takes min(RNE(y), 2) up to 3 and 4
+    above."""
+    if n == 6:
+        m = np.where(y < 2, f32(2.0 ** 20), np.where(y < 4, f32(2.0 ** 21), f32(2.0 ** 22)))
+        return np.minimum(((y + m).astype(f32) - m).astype(f32), f32(7.5))
+    q = np.minimum(((y + f32(2.0 ** 23)).astype(f32) - f32(2.0 ** 23)).astype(f32), f32(2))
+    return np.where(y > 3, f32(4), q).astype(f32)
+
+
+def fpn_value_plain(n, y):
+    """Nearest value of the E2M3 (n = 6) or E2M0 (n = 3) magnitudes, ties to
+    the even code, saturating -- by exhaustive comparison in binary64."""
+    if n == 6:
+        grid = np.array([m / 8 for m in range(8)] + [2.0 ** (e - 1) * (1 + f / 8)
+                                                     for e in (1, 2, 3) for f in range(8)])
+    else:
+        grid = np.array([0.0, 1.0, 2.0, 4.0])
+    yy = np.minimum(y.astype(np.float64), grid[-1] + 1.0)     # far past the top: top
+    d = np.abs(yy[:, None] - grid)
+    m = d.min(1, keepdims=True)
+    tie = d == m
+    even = tie & (np.arange(grid.size) % 2 == 0)
+    k = np.where(even.any(1), even.argmax(1), tie.argmax(1))
+    return grid[k].astype(f32)
+
+
+@pytest.mark.parametrize("n", [3, 6])
+def test_fpn_rounding(n):
+    rng = np.random.default_rng(20 + n)
+    y = np.abs(rng.standard_normal(200_000) * 3).astype(f32)
+    top = 7.5 if n == 6 else 4.0
+    if n == 6:
+        grid = np.array([m / 8 for m in range(8)] + [2.0 ** (e - 1) * (1 + f / 8)
+                                                     for e in (1, 2, 3) for f in range(8)], f32)
+    else:
+        grid = np.array([0.0, 1.0, 2.0, 4.0], f32)
+    mids = ((grid[1:].astype(np.float64) + grid[:-1]) / 2).astype(f32)
+    y = np.concatenate([y, grid, mids, np.nextafter(mids, f32(0)), np.nextafter(mids, f32(99)),
+                        np.array([top + 0.5, 2 * top, 1e30, 2.0 ** -149], f32)])
+    got = fpn_value_kernel(n, y)
+    want = fpn_value_plain(n, y)
+    bad = np.nonzero(got != want)[0]
+    assert bad.size == 0, (y[bad[:5]], got[bad[:5]], want[bad[:5]])
