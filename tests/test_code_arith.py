@@ -168,3 +168,64 @@ def test_fpn_rounding(n):
     want = fpn_value_plain(n, y)
     bad = np.nonzero(got != want)[0]
     assert bad.size == 0, (y[bad[:5]], got[bad[:5]], want[bad[:5]])
+
+
+def e4m3_round_kernel(t):
+    """The kernels' E4M3 rounding of t >= 0 (pattern, ties to even,
+    saturating at 448 = 0x7E): scaled RNE below 2^-6, otherwise rounding the
+    23-bit mantissa to 3 bits with one integer add."""
+    t = t.astype(f32)
+    u = t.view(np.uint32).astype(np.uint64)
+    u = u + np.uint64(0x7FFFF) + ((u >> np.uint64(20)) & np.uint64(1))
+    normal = ((u >> np.uint64(20)) - np.uint64(120 << 3)).astype(np.int64)
+    ts = np.minimum(t, f32(2.0 ** -6))                    # the subnormal branch's inputs
+    sub = np.rint((ts * f32(512)).astype(f32).astype(np.float64)).astype(np.int64)
+    return np.where(t >= 448, 0x7E, np.where(t < 2.0 ** -6, sub, normal))
+
+
+def e4m3_round_plain(t):
+    vals = np.array([(m / 8) * 2.0 ** -6 if e == 0 else (1 + m / 8) * 2.0 ** (e - 7)
+                     for e in range(16) for m in range(8)][:0x7F])
+    tt = np.minimum(t.astype(np.float64), 448.0)
+    d = np.abs(tt[:, None] - vals)
+    m = d.min(1, keepdims=True)
+    tie = d == m
+    even = tie & (np.arange(vals.size) % 2 == 0)
+    return np.where(even.any(1), even.argmax(1), tie.argmax(1))
+
+
+def test_e4m3_rounding():
+    rng = np.random.default_rng(30)
+    vals = np.array([(m / 8) * 2.0 ** -6 if e == 0 else (1 + m / 8) * 2.0 ** (e - 7)
+                     for e in range(16) for m in range(8)][:0x7F], f32)
+    mids = ((vals[1:].astype(np.float64) + vals[:-1]) / 2).astype(f32)
+    t = np.concatenate([np.exp2(rng.uniform(-12, 10, 100_000)).astype(f32), vals, mids,
+                        np.nextafter(mids, f32(0)), np.nextafter(mids, f32(1e9)),
+                        np.array([0.0, 2.0 ** -149, 2.0 ** -10, 447.9, 448.0, 464.0, 480.0, 1e30], f32)])
+    got = e4m3_round_kernel(t)
+    want = e4m3_round_plain(t)
+    bad = np.nonzero(got != want)[0]
+    assert bad.size == 0, (t[bad[:5]], got[bad[:5]], want[bad[:5]])
+
+
+def e2m1_kernel(y):
+    m = np.where(y < 2, f32(2.0 ** 22), np.where(y < 4, f32(2.0 ** 23), f32(2.0 ** 24)))
+    return np.minimum(((y + m).astype(f32) - m).astype(f32), f32(6))
+
+
+def test_e2m1_rounding():
+    grid = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0], f32)
+    mids = ((grid[1:].astype(np.float64) + grid[:-1]) / 2).astype(f32)
+    rng = np.random.default_rng(31)
+    y = np.concatenate([np.abs(rng.standard_normal(200_000) * 3).astype(f32), grid, mids,
+                        np.nextafter(mids, f32(0)), np.nextafter(mids, f32(99)),
+                        np.array([6.5, 7.0, 100.0, 1e30, 2.0 ** -149], f32)])
+    yy = np.minimum(y.astype(np.float64), 7.0)
+    d = np.abs(yy[:, None] - grid)
+    m = d.min(1, keepdims=True)
+    tie = d == m
+    even = tie & (np.arange(8) % 2 == 0)
+    want = grid[np.where(even.any(1), even.argmax(1), tie.argmax(1))]
+    got = e2m1_kernel(y)
+    bad = np.nonzero(got != want)[0]
+    assert bad.size == 0, (y[bad[:5]], got[bad[:5]], want[bad[:5]])
